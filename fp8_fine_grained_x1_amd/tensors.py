@@ -1,0 +1,99 @@
+"""Tensor-level helpers over the C ABI: allocate outputs with torch on the
+inputs' device and call the binding.  No arithmetic happens here.
+
+Layouts (row-major, last index contiguous):
+  quantize_1x128(x [M][K])            -> q u8 [M][K],  s f32 [M][K/128]
+  quantize_128x1(x [T][F])            -> qT u8 [F][T], sT f32 [F][T/128]
+  requantize_128x1(q [T][F], s [T][F/128]) -> same as quantize_128x1
+  quantize_block(w [K][N], transpose) -> q u8 [N][K] (transpose) or [K][N],
+                                         s f32 [K/128][N/128]
+  gemm(qa [M][K], sa [M][K/128], qb [N][K], sb)  -> c [M][N]
+       sb [K/128][N/128] (block scales) or [N][K/128] (per-column scales)
+  grouped_gemm(qa, sa, offsets i32 [G+1], qb [G][N][K], sb [G][K/128][N/128])
+"""
+
+import torch
+
+from . import binding as B
+
+_XTYPE = {torch.bfloat16: B.FP8FG_BF16, torch.float32: B.FP8FG_F32}
+_CTYPE = {torch.bfloat16: B.FP8FG_BF16, torch.float32: B.FP8FG_F32}
+
+
+def _rule(pow2):
+    return B.FP8FG_SCALE_POW2 if pow2 else B.FP8FG_SCALE_AMAX
+
+
+def quantize_1x128(x, pow2=False, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    B.fp8_quantize_rowtile(x, _XTYPE[x.dtype], M, K, x.stride(0), None, 0, 0,
+                           B.FP8FG_TILE_1x128, _rule(pow2), q, q.stride(0), s, s.stride(0), 1,
+                           stream)
+    return q, s
+
+
+def quantize_128x1(x, pow2=False, stream=None):
+    T, F = x.shape
+    qt = torch.empty((F, T), dtype=torch.uint8, device=x.device)
+    st = torch.empty((F, T // 128), dtype=torch.float32, device=x.device)
+    B.fp8_quantize_rowtile(x, _XTYPE[x.dtype], T, F, x.stride(0), None, 0, 0,
+                           B.FP8FG_TILE_128x1, _rule(pow2), qt, qt.stride(0), st, st.stride(0), 1,
+                           stream)
+    return qt, st
+
+
+def requantize_128x1(q, s, pow2=False, stream=None):
+    T, F = q.shape
+    qt = torch.empty((F, T), dtype=torch.uint8, device=q.device)
+    st = torch.empty((F, T // 128), dtype=torch.float32, device=q.device)
+    B.fp8_quantize_rowtile(q, B.FP8FG_E4M3, T, F, q.stride(0), s, s.stride(0), s.stride(1),
+                           B.FP8FG_TILE_128x1, _rule(pow2), qt, qt.stride(0), st, st.stride(0), 1,
+                           stream)
+    return qt, st
+
+
+def quantize_block(w, pow2=False, transpose=True, stream=None):
+    K, N = w.shape
+    shape = (N, K) if transpose else (K, N)
+    q = torch.empty(shape, dtype=torch.uint8, device=w.device)
+    s = torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device)
+    B.fp8_quantize_block(w, _XTYPE[w.dtype], K, N, w.stride(0), _rule(pow2), int(transpose), q,
+                         q.stride(0), s, s.stride(0), s.stride(1), stream)
+    return q, s
+
+
+def gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16, col_scales=False, no_promotion=False,
+         out=None, stream=None):
+    """col_scales=False: sb [K/128][N/128] block scales; True: sb [N][K/128]."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    if col_scales:
+        sb_ns, sb_ks = sb.stride(0), sb.stride(1)
+        mode = B.FP8FG_BSCALE_COL
+    else:
+        sb_ns, sb_ks = sb.stride(1), sb.stride(0)
+        mode = B.FP8FG_BSCALE_BLOCK128
+    if no_promotion:
+        # per-tensor scales broadcast with zero strides
+        sa_ms, sa_ks, sb_ns, sb_ks = 0, 0, 0, 0
+    else:
+        sa_ms, sa_ks = sa.stride(0), sa.stride(1)
+    B.fp8_gemm_blockscaled(M, N, K, qa, qa.stride(0), sa, sa_ms, sa_ks, qb, qb.stride(0), sb,
+                           sb_ns, sb_ks, mode, c, _CTYPE[c.dtype], c.stride(0),
+                           B.FP8FG_GEMM_NO_PROMOTION if no_promotion else B.FP8FG_GEMM_DEFAULT,
+                           stream)
+    return c
+
+
+def grouped_gemm(qa, sa, offsets, qb, sb, out_dtype=torch.bfloat16, out=None, stream=None):
+    M, K = qa.shape
+    G, N, _ = qb.shape
+    c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    B.fp8_grouped_gemm_blockscaled(G, offsets, M, N, K, qa, qa.stride(0), sa, sa.stride(0),
+                                   sa.stride(1), qb, qb.stride(1), qb.stride(0), sb, sb.stride(2),
+                                   sb.stride(1), sb.stride(0), c, _CTYPE[c.dtype], c.stride(0),
+                                   B.FP8FG_GEMM_DEFAULT, stream)
+    return c

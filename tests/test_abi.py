@@ -1,0 +1,178 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry
+point the header declares, and rejects invalid arguments with the
+documented status before touching a device (no GPU needed: every check
+runs on the host before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_fine_grained_x1_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8fg.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from fp8_fine_grained_x1_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"FP8FG_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    assert sorted(declared_functions()) == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_declared_symbols_are_exported(lib):
+    # the shared object exports exactly the C ABI (everything else is hidden)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    text_syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert text_syms == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert B.status_string(st)
+    assert B.status_string(99) == "unknown status"
+
+
+# Fake but well-aligned device addresses: validation must reject the calls
+# below before any of these is dereferenced or any HIP call is made.
+P16 = 1 << 20
+
+
+def rowtile(**kw):
+    args = dict(x=P16, x_type=B.FP8FG_BF16, rows=128, cols=256, ldx=256, x_scale=None, xs_rs=0,
+                xs_ts=0, tile=B.FP8FG_TILE_1x128, scale_rule=B.FP8FG_SCALE_AMAX, q=P16, ldq=256,
+                s=P16, s_rs=2, s_ts=1, stream=0, check=False)
+    args.update(kw)
+    return B.fp8_quantize_rowtile(**args)
+
+
+def block(**kw):
+    args = dict(w=P16, w_type=B.FP8FG_BF16, rows=256, cols=128, ldw=128,
+                scale_rule=B.FP8FG_SCALE_AMAX, transpose_out=1, q=P16, ldq=256, s=P16, s_rs=1,
+                s_cs=1, stream=0, check=False)
+    args.update(kw)
+    return B.fp8_quantize_block(**args)
+
+
+def gemm(**kw):
+    args = dict(M=64, N=128, K=256, a=P16, lda=256, sa=P16, sa_ms=2, sa_ks=1, b=P16, ldb=256,
+                sb=P16, sb_ns=1, sb_ks=1, b_scale_mode=B.FP8FG_BSCALE_BLOCK128, c=P16,
+                c_type=B.FP8FG_BF16, ldc=128, flags=0, stream=0, check=False)
+    args.update(kw)
+    return B.fp8_gemm_blockscaled(**args)
+
+
+def grouped(**kw):
+    args = dict(G=2, offsets=P16, M_total=64, N=128, K=256, a=P16, lda=256, sa=P16, sa_ms=2,
+                sa_ks=1, b=P16, ldb=256, b_gs=128 * 256, sb=P16, sb_ns=1, sb_ks=1, sb_gs=2,
+                c=P16, c_type=B.FP8FG_BF16, ldc=128, flags=0, stream=0, check=False)
+    args.update(kw)
+    return B.fp8_grouped_gemm_blockscaled(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_type=7), B.FP8FG_EINVAL),
+    (dict(tile=5), B.FP8FG_EINVAL),
+    (dict(scale_rule=2), B.FP8FG_EINVAL),
+    (dict(rows=-1), B.FP8FG_EINVAL),
+    (dict(s_rs=-1), B.FP8FG_EINVAL),
+    (dict(cols=200, ldx=256), B.FP8FG_ESHAPE),
+    (dict(tile=B.FP8FG_TILE_128x1, rows=100), B.FP8FG_ESHAPE),
+    (dict(x=None), B.FP8FG_EINVAL),
+    (dict(q=None), B.FP8FG_EINVAL),
+    (dict(s=None), B.FP8FG_EINVAL),
+    (dict(ldx=128), B.FP8FG_ESHAPE),
+    (dict(ldq=128), B.FP8FG_ESHAPE),
+    (dict(x=P16 + 8), B.FP8FG_EALIGN),
+    (dict(q=P16 + 4), B.FP8FG_EALIGN),
+    (dict(s=P16 + 2), B.FP8FG_EALIGN),
+    (dict(ldx=260), B.FP8FG_EALIGN),
+    (dict(ldq=264), B.FP8FG_EALIGN),
+    (dict(x_type=B.FP8FG_E4M3, x_scale=P16), B.FP8FG_EUNSUPPORTED),     # requant is 128x1 only
+    (dict(x_type=B.FP8FG_E4M3, tile=B.FP8FG_TILE_128x1, ldq=128), B.FP8FG_EINVAL),  # no scales
+    (dict(tile=B.FP8FG_TILE_128x1, ldq=64), B.FP8FG_ESHAPE),          # ldq < rows (transposed)
+    (dict(rows=0), B.FP8FG_OK),                                       # empty: no-op
+    (dict(rows=0, x=None, q=None, s=None), B.FP8FG_OK),
+])
+def test_rowtile_validation(lib, kw, status):
+    assert rowtile(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_type=B.FP8FG_E4M3), B.FP8FG_EINVAL),
+    (dict(transpose_out=2), B.FP8FG_EINVAL),
+    (dict(rows=200), B.FP8FG_ESHAPE),
+    (dict(cols=100, ldw=128), B.FP8FG_ESHAPE),
+    (dict(ldq=128), B.FP8FG_ESHAPE),                   # transposed output needs ldq >= rows
+    (dict(transpose_out=0, ldq=64), B.FP8FG_ESHAPE),
+    (dict(w=P16 + 2), B.FP8FG_EALIGN),
+    (dict(w_type=B.FP8FG_F32, ldw=130), B.FP8FG_EALIGN),
+    (dict(s=None), B.FP8FG_EINVAL),
+    (dict(cols=0), B.FP8FG_OK),
+])
+def test_block_validation(lib, kw, status):
+    assert block(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(b_scale_mode=3), B.FP8FG_EINVAL),
+    (dict(c_type=B.FP8FG_E4M3), B.FP8FG_EINVAL),
+    (dict(flags=4), B.FP8FG_EINVAL),
+    (dict(M=-1), B.FP8FG_EINVAL),
+    (dict(sa_ms=-2), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_NO_PROMOTION), B.FP8FG_EINVAL),   # per-K scales with no promotion
+    (dict(K=200, lda=256, ldb=256), B.FP8FG_ESHAPE),
+    (dict(N=100, ldc=128), B.FP8FG_ESHAPE),
+    (dict(lda=128), B.FP8FG_ESHAPE),
+    (dict(ldc=64), B.FP8FG_ESHAPE),
+    (dict(a=None), B.FP8FG_EINVAL),
+    (dict(sb=None), B.FP8FG_EINVAL),
+    (dict(c=None), B.FP8FG_EINVAL),
+    (dict(a=P16 + 8), B.FP8FG_EALIGN),
+    (dict(ldb=264), B.FP8FG_EALIGN),
+    (dict(c=P16 + 1), B.FP8FG_EALIGN),
+    (dict(c_type=B.FP8FG_F32, c=P16 + 2), B.FP8FG_EALIGN),
+    (dict(M=0), B.FP8FG_OK),
+])
+def test_gemm_validation(lib, kw, status):
+    assert gemm(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=-1), B.FP8FG_EINVAL),
+    (dict(G=0), B.FP8FG_EINVAL),                         # rows but no experts
+    (dict(G=0, M_total=0), B.FP8FG_OK),
+    (dict(offsets=None), B.FP8FG_EINVAL),
+    (dict(offsets=P16 + 2), B.FP8FG_EALIGN),
+    (dict(b_gs=100), B.FP8FG_EALIGN),
+    (dict(b_gs=-16), B.FP8FG_EINVAL),
+    (dict(K=100), B.FP8FG_ESHAPE),
+    (dict(M_total=0), B.FP8FG_OK),
+])
+def test_grouped_validation(lib, kw, status):
+    assert grouped(**kw) == status
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(B.Fp8fgError) as ei:
+        B.fp8_quantize_rowtile(P16, 9, 1, 128, 128, None, 0, 0, 0, 0, P16, 128, P16, 1, 1, 0)
+    assert ei.value.status == B.FP8FG_EINVAL

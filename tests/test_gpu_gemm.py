@@ -1,0 +1,298 @@
+"""GPU parity of the block-scaled GEMMs against the CPU oracle.
+
+The quantized operands are checked bit for bit first; the FP32 result must
+satisfy rel_frob <= 1e-5 and max_rel <= 1e-3 (|ref| > 1e-2 rms) against the
+oracle's float64 value; the BF16 result must equal RNE of the same kernel's
+FP32 result and lie within one bf16 ulp of RNE(oracle).  Full-size
+workloads are checked on sampled rows x sampled 128-column blocks that the
+oracle computes exactly; the small cases span several tiles and ragged
+tails and are checked entirely."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_fine_grained_x1_amd import binding as B
+from fp8_fine_grained_x1_amd import tensors as T
+from fp8_fine_grained_x1_amd import workloads
+from gpu_util import (DEV, bf16_dev, check_bf16_output, check_gemm, f32, f32_dev, host, say,
+                      workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def rand_bits(rows, cols, seed, std=1.0, outliers=0.0, mult=1.0, uniform=False):
+    rng = np.random.default_rng(seed)
+    if uniform:
+        x = (rng.random((rows, cols), dtype=np.float32) * 2 - 1).astype(np.float32)
+    else:
+        x = (rng.standard_normal((rows, cols)) * std).astype(np.float32)
+    if outliers:
+        x.flat[rng.choice(x.size, size=max(1, int(outliers * x.size)), replace=False)] *= np.float32(mult)
+    return workloads.f32_to_bf16_bits(x)
+
+
+def dense_case(a_bits, b_bits, a_pow2=False, b_pow2=False, what=""):
+    """Quantize on the GPU, check bytes, run both output types, compare."""
+    ra = oracle.SCALE_POW2 if a_pow2 else oracle.SCALE_AMAX
+    rb = oracle.SCALE_POW2 if b_pow2 else oracle.SCALE_AMAX
+    qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=a_pow2)
+    qb, sb = T.quantize_block(bf16_dev(b_bits), pow2=b_pow2, transpose=True)
+    qao, sao = oracle.quantize_1x128(f32(a_bits), ra)
+    qbo, sbo = oracle.quantize_128x128(f32(b_bits), rb)
+    assert np.array_equal(host(qa), qao) and np.array_equal(host(sa), sao)
+    assert np.array_equal(host(qb), qbo.T) and np.array_equal(host(sb), sbo)
+    c32 = T.gemm(qa, sa, qb, sb, out_dtype=torch.float32)
+    c16 = T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16)
+    ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+    h32 = host(c32)
+    check_gemm(h32, ref, what)
+    check_bf16_output(host(c16), h32, ref)
+    return h32, ref
+
+
+def test_workload1_full():
+    w = workload(1)
+    dense_case(w["A"], w["B"], what="workload 1")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 640), (129, 256, 256),
+                                   (64, 1024, 1152), (513, 640, 384)])
+def test_dense_ragged(M, N, K):
+    a = rand_bits(M, K, seed=M + K, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=N + K, std=0.02)
+    dense_case(a, b, what="M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_dense_pow2_both_operands_k128_fidelity():
+    # with power-of-two scales and K = 128 the oracle value is exact; the gap is
+    # the matrix core's internal summation plus one FP32 promotion
+    a = rand_bits(256, 128, seed=1, outliers=0.01, mult=50)
+    b = rand_bits(128, 256, seed=2, std=0.02)
+    h32, ref = dense_case(a, b, a_pow2=True, b_pow2=True, what="K=128 pow2")
+    err = np.abs(h32 - ref) / np.maximum(np.abs(ref), 1e-30)
+    say("K=128 pow2: max rel err %.3e (median %.3e)" % (err.max(), np.median(err)))
+
+
+def test_identity_weights_bit_exact():
+    M, K = 200, 384
+    a = rand_bits(M, K, seed=4, outliers=0.01, mult=50)
+    qa, sa = T.quantize_1x128(bf16_dev(a))
+    eye = torch.eye(K, dtype=torch.bfloat16, device=DEV)
+    qb, sb = T.quantize_block(eye, pow2=True, transpose=True)
+    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+    qao, sao = oracle.quantize_1x128(f32(a))
+    expect = (oracle.decode(qao).astype(np.float32) * np.repeat(sao, 128, axis=1)).astype(np.float32)
+    assert np.array_equal(c32, expect)
+
+
+def test_strided_output_and_guard_bands():
+    M, N, K = 130, 256, 384
+    a = rand_bits(M, K, seed=8)
+    b = rand_bits(K, N, seed=9, std=0.02)
+    qa, sa = T.quantize_1x128(bf16_dev(a))
+    qb, sb = T.quantize_block(bf16_dev(b))
+    cbuf = torch.full((M + 2, N + 64), 12345.0, dtype=torch.float32, device=DEV)
+    c = cbuf[1:M + 1, 32:32 + N]
+    T.gemm(qa, sa, qb, sb, out=c)
+    hb = host(cbuf)
+    mask = np.ones_like(hb, dtype=bool)
+    mask[1:M + 1, 32:32 + N] = False
+    assert np.all(hb[mask] == 12345.0)
+    ref = oracle.gemm_blockscaled(*oracle.quantize_1x128(f32(a)), *oracle.quantize_128x128(f32(b)))
+    check_gemm(hb[1:M + 1, 32:32 + N], ref, "strided")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 128, 256), (384, 512, 640)])
+def test_column_scales(M, N, K):
+    # Wgrad layout: both operands 128x1-quantized along K (the token axis)
+    x = rand_bits(K, M, seed=M + 1)        # X [T=K][F=M]
+    dy = rand_bits(K, N, seed=N + 2)       # dY [T=K][N]
+    qx, sx = T.quantize_128x1(bf16_dev(x))      # [M][K], [M][K/128]
+    qd, sd = T.quantize_128x1(bf16_dev(dy))     # [N][K], [N][K/128]
+    c32 = host(T.gemm(qx, sx, qd, sd, out_dtype=torch.float32, col_scales=True))
+    qxo, sxo = oracle.quantize_128x1(f32(x))
+    qdo, sdo = oracle.quantize_128x1(f32(dy))
+    assert np.array_equal(host(qx), qxo.T) and np.array_equal(host(sd), sdo.T)
+    check_gemm(c32, oracle.wgrad(qxo, sxo, qdo, sdo), "colscale")
+
+
+def test_no_promotion_per_tensor():
+    M, N, K = 128, 256, 1024
+    a = rand_bits(M, K, seed=21, uniform=True)
+    b = rand_bits(K, N, seed=22, uniform=True)
+    qao, s_a = oracle.quantize_per_tensor(f32(a))
+    qbo, s_b = oracle.quantize_per_tensor(f32(b))
+    qa = torch.from_numpy(qao).to(DEV)
+    qb = torch.from_numpy(np.ascontiguousarray(qbo.T)).to(DEV)
+    sa = torch.tensor([s_a], dtype=torch.float32, device=DEV)
+    sb = torch.tensor([s_b], dtype=torch.float32, device=DEV)
+    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, no_promotion=True))
+    check_gemm(c32, oracle.gemm_per_tensor(qao, s_a, qbo, s_b), "no-promotion")
+
+
+# ---------------------------------------------------------------- grouped
+def grouped_case(counts, N, K, seed, what):
+    counts = np.asarray(counts, np.int64)
+    G, M = len(counts), int(counts.sum())
+    off = workloads.moe_offsets(counts)
+    a = rand_bits(M, K, seed=seed)
+    ws = [rand_bits(K, N, seed=seed + 1 + e, std=0.02) for e in range(G)]
+    qa, sa = T.quantize_1x128(bf16_dev(a), pow2=True)
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    sb = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device=DEV)
+    for e in range(G):
+        q, s = T.quantize_block(bf16_dev(ws[e]))
+        qb[e].copy_(q)
+        sb[e].copy_(s)
+    offs = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    c32 = host(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32))
+    c16 = host(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.bfloat16))
+    qao, sao = oracle.quantize_1x128(f32(a), oracle.SCALE_POW2)
+    qbs, sbs = zip(*[oracle.quantize_128x128(f32(w)) for w in ws])
+    ref = oracle.grouped_gemm_blockscaled(qao, sao, off, qbs, sbs)
+    check_gemm(c32, ref, what)
+    check_bf16_output(c16, c32, ref)
+    return qa, sa, offs, qb, sb, c32
+
+
+def test_grouped_ragged_and_empty_experts():
+    grouped_case([0, 5, 130, 0, 257, 1, 128], N=256, K=384, seed=30, what="grouped ragged")
+
+
+def test_grouped_single_expert_equals_dense():
+    qa, sa, offs, qb, sb, c32 = grouped_case([300], N=384, K=512, seed=40, what="grouped G=1")
+    dense = host(T.gemm(qa, sa, qb[0], sb[0], out_dtype=torch.float32))
+    assert np.array_equal(c32, dense)
+
+
+def test_grouped_all_rows_in_last_expert():
+    grouped_case([0, 0, 0, 200], N=128, K=256, seed=50, what="grouped last")
+
+
+# ---------------------------------------------------------------- full size
+def sample_rows(M, seed, n=40):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    pick |= {0, M - 1, min(127, M - 1), min(128, M - 1)}
+    return np.array(sorted(pick))
+
+
+def sample_blocks(N, seed):
+    rng = np.random.default_rng(seed + 1000)
+    return sorted({0, N // 128 - 1, int(rng.integers(N // 128))})
+
+
+def dense_full_size(w, pow2_a=False):
+    d = workload(w)
+    a_bits, b_bits = d["A"], d["B"]
+    M, K = a_bits.shape
+    N = b_bits.shape[1]
+    say("workload %d: M=%d N=%d K=%d" % (w, M, N, K))
+    qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=pow2_a)
+    qb, sb = T.quantize_block(bf16_dev(b_bits))
+    c32 = T.gemm(qa, sa, qb, sb, out_dtype=torch.float32)
+    c16 = T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16)
+    rows = sample_rows(M, w)
+    qao, sao = oracle.quantize_1x128(f32(a_bits[rows]))
+    idx = torch.from_numpy(rows).to(DEV)
+    h32 = host(c32.index_select(0, idx))
+    h16 = host(c16.index_select(0, idx))
+    for blk in sample_blocks(N, w):
+        cols = slice(blk * 128, (blk + 1) * 128)
+        qbo, sbo = oracle.quantize_128x128(f32(b_bits[:, cols]))
+        ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+        check_gemm(h32[:, cols], ref, "workload %d block %d" % (w, blk))
+        check_bf16_output(h16[:, cols], h32[:, cols], ref)
+    return qa, sa, qb, sb
+
+
+def test_workload2_full_size_sampled():
+    dense_full_size(2)
+
+
+def test_workload3_full_size_sampled_and_naive_gap():
+    dense_full_size(3)
+    # the naive baseline: per-tensor scales, no promotion; compared with its
+    # own oracle, and both compared with the unquantized product
+    d = workload(3)
+    a, b = f32(d["A"]), f32(d["B"])
+    rows = sample_rows(a.shape[0], 33, n=24)
+    cols = slice(0, 256)
+    qao, s_a = oracle.quantize_per_tensor(a)
+    qbo, s_b = oracle.quantize_per_tensor(b)
+    qa = torch.from_numpy(qao).to(DEV)
+    qb = torch.from_numpy(np.ascontiguousarray(qbo.T)).to(DEV)
+    sa = torch.tensor([s_a], dtype=torch.float32, device=DEV)
+    sb = torch.tensor([s_b], dtype=torch.float32, device=DEV)
+    naive = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, no_promotion=True))[rows][:, cols]
+    check_gemm(naive, oracle.gemm_per_tensor(qao[rows], s_a, qbo[:, cols], s_b), "naive vs its oracle")
+    truth = a[rows].astype(np.float64) @ b[:, cols].astype(np.float64)
+    qfa, sfa = T.quantize_1x128(bf16_dev(d["A"]))
+    qfb, sfb = T.quantize_block(bf16_dev(d["B"]))
+    fine = host(T.gemm(qfa, sfa, qfb, sfb, out_dtype=torch.float32))[rows][:, cols]
+    say("K=16384 vs unquantized product: fine-grained rel_frob=%.3e max_rel=%.3e; "
+        "per-tensor no-promotion rel_frob=%.3e max_rel=%.3e" % (
+            oracle.rel_frob(fine, truth), oracle.max_rel(fine, truth),
+            oracle.rel_frob(naive, truth), oracle.max_rel(naive, truth)))
+
+
+def test_workload4_grouped_full_size_sampled():
+    d = workload(4)
+    a_bits, w_bits, counts, off = d["A"], d["W"], d["counts"], d["offsets"]
+    G, K, N = w_bits.shape
+    M = a_bits.shape[0]
+    say("workload 4: G=%d M=%d N=%d K=%d counts=%s" % (G, M, N, K, counts.tolist()))
+    qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=True)
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    sb = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device=DEV)
+    for e in range(G):
+        q, s = T.quantize_block(bf16_dev(w_bits[e]))
+        qb[e].copy_(q)
+        sb[e].copy_(s)
+    offs = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    c32 = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32)
+    c16 = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.bfloat16)
+    rng = np.random.default_rng(44)
+    for e in range(G):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        rows = np.array(sorted({r0, r1 - 1} | set(rng.integers(r0, r1, size=6).tolist())))
+        idx = torch.from_numpy(rows).to(DEV)
+        h32 = host(c32.index_select(0, idx))
+        h16 = host(c16.index_select(0, idx))
+        qao, sao = oracle.quantize_1x128(f32(a_bits[rows]), oracle.SCALE_POW2)
+        for blk in sample_blocks(N, e):
+            cols = slice(blk * 128, (blk + 1) * 128)
+            qbo, sbo = oracle.quantize_128x128(f32(w_bits[e][:, cols]))
+            ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+            check_gemm(h32[:, cols], ref, "workload 4 expert %d block %d" % (e, blk))
+            check_bf16_output(h16[:, cols], h32[:, cols], ref)
+
+
+def test_workload5_wgrad_full_size_sampled():
+    d = workload(5)
+    x_bits, dy_bits = d["X"], d["dY"]
+    Tn, Fn = x_bits.shape
+    N = dy_bits.shape[1]
+    say("workload 5: T=%d F=%d N=%d" % (Tn, Fn, N))
+    qx1, sx1 = T.quantize_1x128(bf16_dev(x_bits))
+    qd1, sd1 = T.quantize_1x128(bf16_dev(dy_bits))
+    qxt, sxt = T.requantize_128x1(qx1, sx1)        # [F][T], [F][T/128]
+    qdt, sdt = T.requantize_128x1(qd1, sd1)        # [N][T], [N][T/128]
+    dw = T.gemm(qxt, sxt, qdt, sdt, out_dtype=torch.float32, col_scales=True)   # [F][N]
+    # oracle: dY fully (its 128x1 tiles span every token), X on sampled slabs
+    qd1o, sd1o = oracle.quantize_1x128(f32(dy_bits))
+    qdo, sdo = oracle.requantize_128x1(qd1o, sd1o)
+    rng = np.random.default_rng(55)
+    for slab in sorted({0, Fn // 128 - 1, int(rng.integers(Fn // 128))}):
+        fs = slice(slab * 128, (slab + 1) * 128)
+        qx1o, sx1o = oracle.quantize_1x128(f32(x_bits[:, fs]))
+        qxo, sxo = oracle.requantize_128x1(qx1o, sx1o)
+        assert np.array_equal(host(qxt[fs]), qxo.T)
+        f_pick = np.array(sorted({0, 127} | set(rng.integers(0, 128, size=10).tolist())))
+        ref = oracle.wgrad(qxo[:, f_pick], sxo[:, f_pick], qdo, sdo)
+        idx = torch.from_numpy(slab * 128 + f_pick).to(DEV)
+        check_gemm(host(dw.index_select(0, idx)), ref, "workload 5 slab %d" % slab)

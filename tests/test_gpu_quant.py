@@ -1,0 +1,245 @@
+"""GPU parity of the quantizers against the CPU oracle: FP8 bytes and
+scales must match bit for bit.  Every call goes through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_fine_grained_x1_amd import binding as B
+from fp8_fine_grained_x1_amd import tensors as T
+from fp8_fine_grained_x1_amd import workloads
+from gpu_util import DEV, bf16_dev, f32, f32_dev, host, say, workload
+
+pytestmark = pytest.mark.gpu
+
+RULES = [(False, oracle.SCALE_AMAX), (True, oracle.SCALE_POW2)]
+
+
+def rand_bf16(rows, cols, seed, outliers=0.01, mult=50.0, scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32) * np.float32(scale)
+    if outliers:
+        k = max(1, int(outliers * x.size))
+        x.flat[rng.choice(x.size, size=k, replace=False)] *= np.float32(mult)
+    return workloads.f32_to_bf16_bits(x)
+
+
+def codec_points():
+    """fp32 values where E4M3 rounding decisions happen: every code, every
+    midpoint between neighbouring codes and the fp32 neighbours of both,
+    values just above 448, tiny and subnormal values, signed zeros."""
+    mags = oracle.code_magnitudes()
+    pts = [0.0, -0.0]
+    for i in range(127):
+        m = np.float32(mags[i])
+        pts += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1000))]
+        if i < 126:
+            mid = np.float32((mags[i] + mags[i + 1]) / 2)
+            pts += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1000))]
+    pts += [448.0, 447.99997, 2.0 ** -10, 2.0 ** -11, 1e-20, 1e-38, 1e-40, 1.4e-45]
+    p = np.array(pts, dtype=np.float32)
+    p = p[np.abs(p) <= 448.0]
+    return np.concatenate([p, -p])
+
+
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_1x128_codec_points_f32(pow2, rule):
+    # each tile holds +-448 (so s == 1 under both rules) and 127 probe values
+    pts = codec_points()
+    n = (len(pts) + 126) // 127
+    pts = np.concatenate([pts, np.zeros(n * 127 - len(pts), np.float32)])
+    x = np.empty((n, 128), np.float32)
+    x[:, 0] = np.where(np.arange(n) % 2 == 0, 448.0, -448.0)
+    x[:, 1:] = pts.reshape(n, 127)
+    q, s = T.quantize_1x128(f32_dev(x), pow2=pow2)
+    qo, so = oracle.quantize_1x128(x, rule)
+    assert np.all(so == 1.0)
+    assert np.array_equal(host(s), so)
+    bad = np.flatnonzero(host(q) != qo)
+    assert bad.size == 0, [(float(x.flat[i]), int(host(q).flat[i]), int(qo.flat[i])) for i in bad[:8]]
+
+
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_1x128_random_f32_tiles(pow2, rule):
+    # random fp32 data of widely varying magnitude: exercises the division,
+    # the fp32 quotient that can exceed 448 by one ulp, and the clamp
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((2048, 512)) * 10.0 ** rng.uniform(-30, 30, (2048, 1))).astype(np.float32)
+    q, s = T.quantize_1x128(f32_dev(x), pow2=pow2)
+    qo, so = oracle.quantize_1x128(x, rule)
+    assert np.array_equal(host(s), so)
+    assert np.array_equal(host(q), qo)
+
+
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_1x128_every_bf16_pattern(pow2, rule):
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    v = f32(bits)
+    bits = bits[np.isfinite(v)]
+    rng = np.random.default_rng(5)
+    bits = np.concatenate([rng.permutation(bits), rng.permutation(bits)])
+    bits = bits[: (len(bits) // 1024) * 1024].reshape(-1, 1024)
+    q, s = T.quantize_1x128(bf16_dev(bits), pow2=pow2)
+    qo, so = oracle.quantize_1x128(f32(bits), rule)
+    assert np.array_equal(host(s), so)
+    assert np.array_equal(host(q), qo)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 384), (257, 1024), (128, 7168)])
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_1x128_shapes(rows, cols, pow2, rule):
+    bits = rand_bf16(rows, cols, seed=rows * 7 + cols)
+    q, s = T.quantize_1x128(bf16_dev(bits), pow2=pow2)
+    qo, so = oracle.quantize_1x128(f32(bits), rule)
+    assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
+
+
+def test_1x128_strided_views_and_guard_bands():
+    rows, cols = 130, 512
+    bits = rand_bf16(rows, 640, seed=11)
+    x = bf16_dev(bits)[:, 64:64 + cols]                  # ldx = 640 > cols (16-byte aligned)
+    qbuf = torch.full((rows + 2, 768), 0xA5, dtype=torch.uint8, device=DEV)
+    q = qbuf[1:rows + 1, 128:128 + cols]                 # ldq = 768
+    sbuf = torch.full((cols // 128 + 1, rows + 3), -7.0, dtype=torch.float32, device=DEV)
+    s_t = sbuf[:cols // 128, 1:rows + 1]                 # scales stored tile-major: s[t][r]
+    B.fp8_quantize_rowtile(x, B.FP8FG_BF16, rows, cols, x.stride(0), None, 0, 0,
+                           B.FP8FG_TILE_1x128, B.FP8FG_SCALE_AMAX, q, q.stride(0), s_t,
+                           s_t.stride(1), s_t.stride(0))
+    qo, so = oracle.quantize_1x128(f32(bits[:, 64:64 + cols]))
+    qh, sh = host(qbuf), host(sbuf)
+    assert np.array_equal(qh[1:rows + 1, 128:128 + cols], qo)
+    assert np.array_equal(sh[:cols // 128, 1:rows + 1], so.T)
+    # nothing written outside the views
+    qmask = np.ones_like(qh, dtype=bool)
+    qmask[1:rows + 1, 128:128 + cols] = False
+    assert np.all(qh[qmask] == 0xA5)
+    smask = np.ones_like(sh, dtype=bool)
+    smask[:cols // 128, 1:rows + 1] = False
+    assert np.all(sh[smask] == -7.0)
+
+
+def test_1x128_zero_tiny_and_signed_zero_tiles():
+    x = np.zeros((4, 256), np.float32)
+    x[1, :128] = -0.0
+    x[1, 128:] = np.where(np.arange(128) % 2, -1.0, 1.0) * np.float32(2.0 ** -130)
+    x[2, ::2] = -0.0
+    x[3] = np.float32(1e-39) * np.arange(256, dtype=np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    for pow2, rule in RULES:
+        q, s = T.quantize_1x128(bf16_dev(bits), pow2=pow2)
+        qo, so = oracle.quantize_1x128(f32(bits), rule)
+        assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
+
+
+def test_1x128_empty_is_noop():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    q, s = T.quantize_1x128(x)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+# ---------------------------------------------------------------- 128x1
+@pytest.mark.parametrize("rows,cols", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_128x1_direct(rows, cols, pow2, rule):
+    bits = rand_bf16(rows, cols, seed=rows + cols)
+    qt, st = T.quantize_128x1(bf16_dev(bits), pow2=pow2)
+    qo, so = oracle.quantize_128x1(f32(bits), rule)
+    assert np.array_equal(host(st), so.T) and np.array_equal(host(qt), qo.T)
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (256, 640)])
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_128x1_requant(rows, cols, pow2, rule):
+    bits = rand_bf16(rows, cols, seed=3 * rows + cols)
+    q1, s1 = T.quantize_1x128(bf16_dev(bits))
+    qt, st = T.requantize_128x1(q1, s1, pow2=pow2)
+    q1o, s1o = oracle.quantize_1x128(f32(bits))
+    assert np.array_equal(host(q1), q1o) and np.array_equal(host(s1), s1o)
+    qo, so = oracle.requantize_128x1(q1o, s1o, rule)
+    assert np.array_equal(host(st), so.T) and np.array_equal(host(qt), qo.T)
+
+
+def test_128x1_f32_input():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((256, 256)) * 3).astype(np.float32)
+    qt, st = T.quantize_128x1(f32_dev(x))
+    qo, so = oracle.quantize_128x1(x)
+    assert np.array_equal(host(st), so.T) and np.array_equal(host(qt), qo.T)
+
+
+# ---------------------------------------------------------------- 128x128
+@pytest.mark.parametrize("transpose", [True, False])
+@pytest.mark.parametrize("pow2,rule", RULES)
+@pytest.mark.parametrize("rows,cols", [(128, 128), (512, 256), (256, 640)])
+def test_block(rows, cols, transpose, pow2, rule):
+    bits = rand_bf16(rows, cols, seed=rows * 3 + cols, scale=0.02)
+    q, s = T.quantize_block(bf16_dev(bits), pow2=pow2, transpose=transpose)
+    qo, so = oracle.quantize_128x128(f32(bits), rule)
+    assert np.array_equal(host(s), so)
+    assert np.array_equal(host(q), qo.T if transpose else qo)
+
+
+def test_block_f32_and_zero_block():
+    rng = np.random.default_rng(2)
+    w = (rng.standard_normal((256, 256)) * 0.02).astype(np.float32)
+    w[:128, 128:] = 0.0
+    w[128:, :128] = -0.0
+    q, s = T.quantize_block(f32_dev(w))
+    qo, so = oracle.quantize_128x128(w)
+    assert np.array_equal(host(s), so) and np.array_equal(host(q), qo.T)
+
+
+# ---------------------------------------------------------------- full size
+def _rows_sample(M, seed, n=48):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    pick |= {0, M - 1, min(127, M - 1), min(128, M - 1)}
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("w,key,pow2", [(2, "A", False), (3, "A", False), (4, "A", True),
+                                        (5, "X", False), (5, "dY", False)])
+def test_full_size_1x128_sampled_rows(w, key, pow2):
+    bits = workload(w)[key]
+    say("workload %d %s %s 1x128 pow2=%s" % (w, key, bits.shape, pow2))
+    q, s = T.quantize_1x128(bf16_dev(bits), pow2=pow2)
+    rows = _rows_sample(bits.shape[0], seed=w)
+    qo, so = oracle.quantize_1x128(f32(bits[rows]), oracle.SCALE_POW2 if pow2 else oracle.SCALE_AMAX)
+    idx = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(host(s.index_select(0, idx)), so)
+    assert np.array_equal(host(q.index_select(0, idx)), qo)
+
+
+@pytest.mark.parametrize("w,key", [(2, "B"), (3, "B"), (4, "W")])
+def test_full_size_block_sampled(w, key):
+    bits = workload(w)[key]
+    mats = bits if bits.ndim == 3 else bits[None]
+    for e in range(mats.shape[0]):
+        say("workload %d %s[%d] %s block" % (w, key, e, mats[e].shape))
+        q, s = T.quantize_block(bf16_dev(mats[e]))
+        K, N = mats[e].shape
+        rng = np.random.default_rng(e + w)
+        blocks = sorted({0, N // 128 - 1, int(rng.integers(N // 128))})
+        for bcol in blocks:
+            sub = mats[e][:, bcol * 128:(bcol + 1) * 128]
+            qo, so = oracle.quantize_128x128(f32(sub))
+            assert np.array_equal(host(s[:, bcol:bcol + 1]), so)
+            assert np.array_equal(host(q[bcol * 128:(bcol + 1) * 128]), qo.T)
+
+
+@pytest.mark.parametrize("key", ["X", "dY"])
+def test_full_size_requant_128x1_sampled(key):
+    bits = workload(5)[key]
+    Tn, Fn = bits.shape
+    say("workload 5 %s %s 1x128 -> 128x1" % (key, bits.shape))
+    q1, s1 = T.quantize_1x128(bf16_dev(bits))
+    qt, st = T.requantize_128x1(q1, s1)
+    rng = np.random.default_rng(17)
+    for slab in sorted({0, Fn // 128 - 1, int(rng.integers(Fn // 128))}):
+        sub = f32(bits[:, slab * 128:(slab + 1) * 128])
+        q1o, s1o = oracle.quantize_1x128(sub)
+        qo, so = oracle.requantize_128x1(q1o, s1o)
+        assert np.array_equal(host(qt[slab * 128:(slab + 1) * 128]), qo.T)
+        assert np.array_equal(host(st[slab * 128:(slab + 1) * 128]), so.T)
