@@ -54,10 +54,10 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
                       int b_scale_mode, void* c, int c_type, int64_t ldc, int flags) {
   if (b_scale_mode != FP8FG_BSCALE_BLOCK128 && b_scale_mode != FP8FG_BSCALE_COL) return FP8FG_EINVAL;
   if (c_type != FP8FG_BF16 && c_type != FP8FG_F32) return FP8FG_EINVAL;
-  if (flags != FP8FG_GEMM_DEFAULT && flags != FP8FG_GEMM_NO_PROMOTION) return FP8FG_EINVAL;
+  if (flags & ~(FP8FG_GEMM_NO_PROMOTION | FP8FG_GEMM_FP8_MFMA)) return FP8FG_EINVAL;
   if (M < 0 || N < 0 || K < 0 || lda < 0 || ldb < 0 || ldc < 0) return FP8FG_EINVAL;
   if (sa_ms < 0 || sa_ks < 0 || sb_ns < 0 || sb_ks < 0) return FP8FG_EINVAL;
-  if (flags == FP8FG_GEMM_NO_PROMOTION && (sa_ks != 0 || sb_ks != 0)) return FP8FG_EINVAL;
+  if ((flags & FP8FG_GEMM_NO_PROMOTION) && (sa_ks != 0 || sb_ks != 0)) return FP8FG_EINVAL;
   if (K % 128 || N % 128) return FP8FG_ESHAPE;
   if (M == 0 || N == 0) return FP8FG_OK;
   if (!c || !sa || !sb || (K > 0 && (!a || !b))) return FP8FG_EINVAL;
@@ -153,7 +153,7 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
   if (((M + 127) / 128) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
   fp8fg::GemmArgs g{M,  N,  K,  a,      lda,    sa, sa_ms,
                     sa_ks, b, ldb, sb, sb_ns, sb_ks, b_scale_mode,
-                    c,  c_type, ldc, flags == FP8FG_GEMM_NO_PROMOTION,
+                    c,  c_type, ldc, flags,
                     0,  nullptr, 0,  0};
   return launched(fp8fg::launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -176,7 +176,7 @@ int fp8_grouped_gemm_blockscaled(int64_t G, const int32_t* offsets, int64_t M_to
   if (((M_total + 127) / 128 + G) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
   fp8fg::GemmArgs g{M_total, N,  K,  a,      lda,    sa, sa_ms,
                     sa_ks,   b,  ldb, sb, sb_ns, sb_ks, FP8FG_BSCALE_BLOCK128,
-                    c,       c_type, ldc, flags == FP8FG_GEMM_NO_PROMOTION,
+                    c,       c_type, ldc, flags,
                     G,       offsets, b_gs, sb_gs};
   return launched(fp8fg::launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }

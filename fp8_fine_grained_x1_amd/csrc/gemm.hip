@@ -3,26 +3,45 @@
 // The method ([thedaegu] Figure 7(b) passage; [fooled] promotion paragraph;
 // [hearaon] accumulation-precision paragraph; page keys in
 // include/fp8fg.h): an FP8 GEMM whose operands carry one scale per 128
-// elements of K sums each 128-wide K group in the matrix unit, then
-// promotes that partial sum into a full FP32 accumulator, applying the
+// elements of K forms the partial sum of each 128-wide K group in the
+// matrix unit, then promotes it into a full FP32 accumulator, applying the
 // group's dequantization scales at the same time.
 //
-// gfx950 mapping (not the pages' Hopper design, which overlapped two
-// warpgroups so that one promotes while the other runs MMA):
-//   * one v_mfma_scale_f32_16x16x128_f8f6f4 covers exactly one K group of a
-//     16x16 output tile, so the partial sum P of a K group is a single
-//     instruction issued with a zero accumulator (E8M0 operand scales = 1);
-//   * promotion is acc = fma(P, sa(m,kb) * sb(kb,n), acc) on the VALU, which
-//     the hardware overlaps with the next in-flight MFMAs of the same wave;
+// gfx950 finding that shapes this kernel: the FP8 MFMA instructions
+// (v_mfma_*_f8f6f4 and the older *_fp8_fp8) add the products of every 8
+// consecutive K elements at a precision of about 14 bits below the largest
+// of them (smaller products are cut off), before the 8-product sums are
+// accumulated in FP32.  That is the same kind of limitation the pages
+// measured on Hopper tensor cores, but it sits *inside* one instruction, so
+// no promotion interval can remove it (relative Frobenius error ~5e-5 on
+// the reference workloads).  The BF16 MFMA has no such loss.  Hence:
+//
+// default path (MODE 0, exact partial sums):
+//   * the FP8 tiles stay FP8 in HBM and LDS (half the bytes of BF16);
+//   * each wave converts its fragments FP8 -> BF16 in registers with
+//     v_cvt_scalef32_pk_bf16_fp8 (scale 1.0: exact, every E4M3 value is a
+//     BF16 value) and runs v_mfma_f32_32x32x16_bf16, chaining the 8
+//     16-wide K steps of a K group in one accumulator P;
+//   * promotion acc = fma(P, sa(m,kb) * sb(kb,n), acc) on the VALU, once per
+//     output element and K group.
+// FP8 paths (flags): MODE 1 forms P with one v_mfma_scale_f32_16x16x128_f8f6f4
+//   per 16x16 tile and K group (E8M0 operand scales = 1), then promotes as
+//   above; MODE 2 (no promotion) chains the FP8 MFMA over the whole K and
+//   applies per-tensor scales once -- the naive baseline.
+//
+// Shared structure:
 //   * workgroup tile 128x128, four waves in a 2x2 arrangement, each wave a
-//     64x64 sub-tile = 4x4 MFMA tiles (64 FP32 accumulators per lane);
+//     64x64 sub-tile;
 //   * A and B tiles (128 rows x 128 K bytes each) move HBM/L2 -> LDS with
-//     global_load_lds_dwordx4 (no VGPR staging), double-buffered so the
-//     next K group streams in while the current one is multiplied; rows are
-//     stored with their 16-byte chunks XOR-swizzled by (row % 8) so that
-//     the fragment reads of 8 consecutive rows hit distinct LDS banks;
-//   * per-row scales of A (and per-column scales of B in the column mode)
-//     ride along into LDS with global_load_lds_dword;
+//     global_load_lds_dwordx4 (no VGPR staging), double-buffered so the next
+//     K group streams in while the current one is multiplied; the 16-byte
+//     chunks of each 128-byte row are XOR-swizzled by (row % 8) so that
+//     fragment reads of 8 consecutive rows hit distinct LDS banks;
+//   * per-row scales of A (and per-column scales of B in the column mode) are
+//     loaded into registers two K groups ahead and written into a separate
+//     LDS object one group ahead, so that neither ever waits for the tile
+//     copies in flight; a B block scale is one wave-uniform load per K group,
+//     issued a group ahead;
 //   * workgroup ids are remapped so that consecutive tiles run on the same
 //     XCD (each XCD has its own L2), and tiles are ordered in groups of 8
 //     M-tiles so that co-resident workgroups share A and B panels.
@@ -33,6 +52,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "fp8fg.h"
 #include "launch.h"
 
 namespace fp8fg {
@@ -41,6 +61,9 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128;
 constexpr int kBN = 128;
@@ -49,9 +72,16 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kE8M0One = 127;  // E8M0 encoding of 2^0
 
+constexpr int kModeExact = 0;     // BF16 MFMA partial sums
+constexpr int kModeFp8 = 1;       // FP8 MFMA partial sums, promoted
+constexpr int kModeFp8NoPromo = 2;
+
 struct __align__(16) Stage {
   uint8_t a[kBM * kBK];
   uint8_t b[kBN * kBK];
+};
+// Scales of one K group (A rows; B columns in the per-column mode).
+struct __align__(16) Scales {
   float sa[kBM];
   float sb[kBN];
 };
@@ -80,9 +110,6 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 4, 0, 0);
 }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
@@ -113,9 +140,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)(u >> 16);
 }
 
-template <int CT, int BMODE, bool NOPROMO, bool GROUPED>
+template <int CT>
+__device__ __forceinline__ void store_c(void* c, int64_t idx, float v) {
+  if constexpr (CT == 0) {
+    reinterpret_cast<uint16_t*>(c)[idx] = f32_to_bf16_rne(v);
+  } else {
+    reinterpret_cast<float*>(c)[idx] = v;
+  }
+}
+
+// 8 E4M3 bytes (two dwords) -> 8 BF16 values, exactly.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  union {
+    v2bf p[4];
+    v8bf v;
+  } u;
+  u.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+  u.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+  u.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+  u.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+  return u.v;
+}
+
+template <int CT, int BMODE, int MODE, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p) {
-  __shared__ Stage stage[2];
+  constexpr bool kPromote = MODE != kModeFp8NoPromo;
+  // Two stages of tiles and two of scales, each its own LDS object: with the
+  // K loop unrolled by two every access names its object at compile time, so
+  // the compiler can tell copies in flight into one stage from reads of the
+  // other and inserts no wait between them.
+  __shared__ Stage stage0;
+  __shared__ Stage stage1;
+  __shared__ Scales scales0;
+  __shared__ Scales scales1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,17 +185,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
   const uint8_t* A = p.a;
   const uint8_t* B = p.b;
   const float* SB = p.sb;
-  int64_t row_base;
-  int rows_valid;
-  int tn;
+  int64_t row_base = 0;
+  int rows_valid = 0;
+  int tn = 0;
   if constexpr (GROUPED) {
     int t = id;
     int e = 0;
-    int64_t seg0 = 0, seg1 = 0;
     bool found = false;
     for (; e < p.G; ++e) {
-      seg0 = p.offsets[e];
-      seg1 = p.offsets[e + 1];
+      const int64_t seg0 = p.offsets[e];
+      const int64_t seg1 = p.offsets[e + 1];
       const int tm_e = (int)((seg1 - seg0 + kBM - 1) / kBM);
       const int cnt = tm_e * p.tiles_n;
       if (t < cnt) {
@@ -166,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
   const int64_t n0 = (int64_t)tn * kBN;
   const int nkb = (int)(p.K / kBK);
 
-  // ---- per-lane DMA sources.  Instruction i of wave w fills LDS rows
+  // ---- per-lane copy sources.  Instruction i of wave w fills LDS rows
   // (4i + w) * 8 .. +8; lane l writes physical chunk l % 8 of row l / 8,
   // which holds logical K chunk (l % 8) ^ (row % 8).
   const int lrow = lane >> 3;
@@ -180,169 +236,295 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
     a_src[i] = A + (row_base + ra) * p.lda + lchunk * 16;
     b_src[i] = B + (n0 + r) * p.ldb + lchunk * 16;
   }
+  // scales: lane l of wave 0 (A rows) / wave 1 (B columns) copies entries l, l + 64
   const float* sa_src[2];
+  const float* sbc_src[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = h * 64 + lane;
     const int ra = r < rows_valid ? r : rows_valid - 1;
     sa_src[h] = p.sa + (row_base + ra) * p.sa_ms;
+    sbc_src[h] = SB + (n0 + r) * p.sb_ns;
   }
-  const float* sbc_src[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) sbc_src[h] = SB + (n0 + h * 64 + lane) * p.sb_ns;
 
+  // Copies of K group kb's tiles into stage S (LDS DMA, no VGPRs).
   auto issue = [&](int kb, Stage& S) {
     const int64_t koff = (int64_t)kb * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(a_src[i] + koff, S.a + (i * 4 + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(b_src[i] + koff, S.b + (i * 4 + wave) * 1024);
-    if (!NOPROMO && wave == 0) {
+  };
+  // Scales travel global -> VGPR -> LDS: loaded two K groups ahead (so the
+  // wait at the top of the next group already covers them) and written into
+  // their own LDS object at the end of the group before their use.
+  auto load_scales = [&](int kb, float (&v)[2]) {
+    if (kPromote && wave == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dma4(sa_src[h] + kb * p.sa_ks, S.sa + h * 64);
-    }
-    if (!NOPROMO && BMODE == 1 && wave == 1) {
+      for (int h = 0; h < 2; ++h) v[h] = sa_src[h][(int64_t)kb * p.sa_ks];
+    } else if (kPromote && BMODE == 1 && wave == 1) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dma4(sbc_src[h] + kb * p.sb_ks, S.sb + h * 64);
+      for (int h = 0; h < 2; ++h) v[h] = sbc_src[h][(int64_t)kb * p.sb_ks];
     }
   };
-
-  v4f acc[4][4];
+  auto store_scales = [&](Scales& SC, const float (&v)[2]) {
+    if (kPromote && wave == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int h = 0; h < 2; ++h) SC.sa[h * 64 + lane] = v[h];
+    } else if (kPromote && BMODE == 1 && wave == 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2; ++h) SC.sb[h * 64 + lane] = v[h];
+    }
+  };
+  float scr0[2] = {0.f, 0.f}, scr1[2] = {0.f, 0.f};  // scale registers, two sets
 
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // B block scales: one value per K group for this tile's 128 columns (a
-  // wave-uniform address, read through the scalar cache).
+  // B block scales: one value per K group for this tile's 128 columns
+  // (wave-uniform), loaded one group ahead.
   const float* sb_blk = SB + __builtin_amdgcn_readfirstlane((int)(n0 >> 7)) * p.sb_ns;
 
-  // sbv: block scale of B for the current K group, loaded one group ahead
-  float sbv = 0.f;
-  if (nkb > 0) {
-    issue(0, stage[0]);
-    if (!NOPROMO && BMODE == 0) sbv = sb_blk[0];
-  }
-  for (int kb = 0; kb < nkb; ++kb) {
-    const Stage& S = stage[kb & 1];
-    wait_vmcnt0();   // this wave's copies of K group kb have landed in LDS
-    __syncthreads(); // ... and everyone's; stage (kb+1)&1 is free again
+  if constexpr (MODE == kModeExact) {
+    // ================================================================ BF16 MFMA
+    // Wave tile 64x64 = 2x2 tiles of 32x32.  Lane l serves row/column l % 32
+    // of a tile; lane group g = l / 32 takes K bytes [64 g, 64 g + 64) of each
+    // K group, 8 per 16-wide K step (the same permutation of K for A and B).
+    // Accumulator layout of v_mfma_f32_32x32x16_bf16: element r of lane l is
+    // row 8 (r / 4) + 4 g + r % 4, column l % 32.
+    const int g = lane >> 5;
+    const int lr = lane & 31;
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // ---- fragments: lane l supplies row l % 16 and K bytes [32 (l/16), +32)
-    v8i af[4], bf[4];
+    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx, Scales& NS,
+                     float (&sc_store)[2], float (&sc_load)[2], float& sbv) {
+      wait_vmcnt0();    // this wave's copies of K group kb have landed in LDS
+      __syncthreads();  // ... and everyone's; the other stage is free again
+      float sbv_next = 0.f;
+      if (kb + 1 < nkb) {
+        if (BMODE == 0) sbv_next = sb_blk[(int64_t)(kb + 1) * p.sb_ks];
+        issue(kb + 1, Nx);
+      }
+      if (kb + 2 < nkb) load_scales(kb + 2, sc_load);
+      v16f P[2][2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // raw FP8: 16 bytes per lane and tile = two 16-wide K steps
+        uint4 ra[2], rb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = wm * 64 + i * 32 + lr;
+          ra[i] = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((4 * g + c) ^ (row & 7)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = wn * 64 + j * 32 + lr;
+          rb[j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ (row & 7)) << 4));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          v8bf af[2], bf[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            af[i] = h ? fp8x8_to_bf16(ra[i].z, ra[i].w) : fp8x8_to_bf16(ra[i].x, ra[i].y);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            bf[j] = h ? fp8x8_to_bf16(rb[j].z, rb[j].w) : fp8x8_to_bf16(rb[j].x, rb[j].y);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              if (c == 0 && h == 0) {
+                const v16f z = {};
+                P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], z, 0, 0, 0);
+              } else {
+                P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], P[i][j], 0, 0, 0);
+              }
+            }
+        }
+      }
+      // promotion: the row scales of this lane are tile i, rows 8 q + 4 g + t
+      float sbc[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 32 + lr] : sbv;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 s4 = *reinterpret_cast<const float4*>(SS.sa + wm * 64 + i * 32 + 8 * q + 4 * g);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float s[4] = {s4.x * sbc[j], s4.y * sbc[j], s4.z * sbc[j], s4.w * sbc[j]};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t], s[t], acc[i][j][4 * q + t]);
+          }
+        }
+      if (kb + 1 < nkb) store_scales(NS, sc_store);
+      sbv = sbv_next;
+    };
+
+    float sbv = 0.f;
+    if (nkb > 0) {
+      if (BMODE == 0) sbv = sb_blk[0];
+      load_scales(0, scr0);
+      if (nkb > 1) load_scales(1, scr1);
+      store_scales(scales0, scr0);
+      issue(0, stage0);
+    }
+    for (int kb = 0; kb < nkb; kb += 2) {
+      group(kb, stage0, scales0, stage1, scales1, scr1, scr0, sbv);
+      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scales0, scr0, scr1, sbv);
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t col = n0 + wn * 64 + j * 32 + lr;
+          store_c<CT>(p.c, grow * p.ldc + col, acc[i][j][r]);
+        }
+      }
+  } else {
+    // ================================================================ FP8 MFMA
+    // Wave tile 64x64 = 4x4 tiles of 16x16.  Lane l supplies row l % 16 and K
+    // bytes [32 (l/16), +32) of a K group; accumulator element r of lane l is
+    // row 4 (l/16) + r, column l % 16.
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int fr = lane & 15;
     const int fc = (lane >> 4) * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 64 + i * 16 + fr;
-      const int sw = row & 7;
-      const uint4 lo = *reinterpret_cast<const uint4*>(S.a + row * 128 + ((fc ^ sw) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((fc + 1) ^ sw) << 4));
-      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wn * 64 + j * 16 + fr;
-      const int sw = row & 7;
-      const uint4 lo = *reinterpret_cast<const uint4*>(S.b + row * 128 + ((fc ^ sw) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((fc + 1) ^ sw) << 4));
-      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    // output rows of this lane within each 16x16 tile: 4 (l/16) + r
-    float sar[4][4];
-    float sbc[4];
-    if constexpr (!NOPROMO) {
+
+    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx, Scales& NS,
+                     float (&sc_store)[2], float (&sc_load)[2], float& sbv) {
+      wait_vmcnt0();
+      __syncthreads();
+      float sbv_next = 0.f;
+      if (kb + 1 < nkb) {
+        if (kPromote && BMODE == 0) sbv_next = sb_blk[(int64_t)(kb + 1) * p.sb_ks];
+        issue(kb + 1, Nx);
+      }
+      if (kb + 2 < nkb) load_scales(kb + 2, sc_load);
+      v8i af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 t = *reinterpret_cast<const float4*>(S.sa + wm * 64 + i * 16 + 4 * (lane >> 4));
-        sar[i][0] = t.x; sar[i][1] = t.y; sar[i][2] = t.z; sar[i][3] = t.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sbc[j] = BMODE == 1 ? S.sb[wn * 64 + j * 16 + fr] : 1.0f;
-    }
-
-    // All reads of this stage are issued above, so the copies of the next
-    // K group (into the other stage) can start now and overlap the MFMAs.
-    float sbv_next = 0.f;
-    if (kb + 1 < nkb) {
-      issue(kb + 1, stage[(kb + 1) & 1]);
-      if (!NOPROMO && BMODE == 0) sbv_next = sb_blk[(int64_t)(kb + 1) * p.sb_ks];
-    }
-
-    if constexpr (NOPROMO) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf[j], acc[i][j], 0, 0, 0, kE8M0One, 0, kE8M0One);
-    } else {
-      if constexpr (BMODE == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sar[i][r] *= sbv;
+        const int row = wm * 64 + i * 16 + fr;
+        const int sw = row & 7;
+        const uint4 lo = *reinterpret_cast<const uint4*>(S.a + row * 128 + ((fc ^ sw) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((fc + 1) ^ sw) << 4));
+        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sbj = sbc[j];
+        const int row = wn * 64 + j * 16 + fr;
+        const int sw = row & 7;
+        const uint4 lo = *reinterpret_cast<const uint4*>(S.b + row * 128 + ((fc ^ sw) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((fc + 1) ^ sw) << 4));
+        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      if constexpr (!kPromote) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[i], bf[j], acc[i][j], 0, 0, 0, kE8M0One, 0, kE8M0One);
+      } else {
+        float sar[4][4];
+        float sbc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf[j], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+          const float4 t = *reinterpret_cast<const float4*>(SS.sa + wm * 64 + i * 16 + 4 * (lane >> 4));
+          sar[i][0] = t.x; sar[i][1] = t.y; sar[i][2] = t.z; sar[i][3] = t.w;
+        }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sc = BMODE == 0 ? sar[i][r] : sar[i][r] * sbj;
-            acc[i][j][r] = __builtin_fmaf(P[r], sc, acc[i][j][r]);
+        for (int j = 0; j < 4; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 16 + fr] : sbv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[i], bf[j], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j][r] = __builtin_fmaf(P[r], sar[i][r] * sbc[j], acc[i][j][r]);
           }
         }
       }
-    }
-    sbv = sbv_next;
-  }
+      if (kb + 1 < nkb) store_scales(NS, sc_store);
+      sbv = sbv_next;
+    };
 
-  // ---- epilogue: lane holds C[4 (l/16) + r][l % 16] of each 16x16 tile
+    float sbv = 0.f;
+    if (nkb > 0) {
+      if (kPromote && BMODE == 0) sbv = sb_blk[0];
+      load_scales(0, scr0);
+      if (nkb > 1) load_scales(1, scr1);
+      store_scales(scales0, scr0);
+      issue(0, stage0);
+    }
+    for (int kb = 0; kb < nkb; kb += 2) {
+      group(kb, stage0, scales0, stage1, scales1, scr1, scr0, sbv);
+      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scales0, scr0, scr1, sbv);
+    }
+
+    // ---- epilogue
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-      if (row >= rows_valid) continue;
-      const int64_t grow = row_base + row;
-      float rs = 1.0f;
-      if constexpr (NOPROMO) rs = p.sa[grow * p.sa_ms];
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+        float rs = 1.0f;
+        if constexpr (!kPromote) rs = p.sa[grow * p.sa_ms];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
-        float v = acc[i][j][r];
-        if constexpr (NOPROMO) {
-          const float cs = BMODE == 0 ? sb_blk[0] : SB[col * p.sb_ns];
-          v = v * (rs * cs);
-        }
-        if constexpr (CT == 0) {
-          reinterpret_cast<uint16_t*>(p.c)[grow * p.ldc + col] = f32_to_bf16_rne(v);
-        } else {
-          reinterpret_cast<float*>(p.c)[grow * p.ldc + col] = v;
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+          float v = acc[i][j][r];
+          if constexpr (!kPromote) {
+            const float cs = BMODE == 0 ? sb_blk[0] : SB[col * p.sb_ns];
+            v = v * (rs * cs);
+          }
+          store_c<CT>(p.c, grow * p.ldc + col, v);
         }
       }
     }
   }
 }
 
-template <int CT, int BMODE, bool NOPROMO, bool GROUPED>
+template <int CT, int BMODE, int MODE, bool GROUPED>
 hipError_t launch_t(const KParams& kp, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_blockscaled_kernel<CT, BMODE, NOPROMO, GROUPED>), dim3(kp.nblocks),
+  hipLaunchKernelGGL((gemm_blockscaled_kernel<CT, BMODE, MODE, GROUPED>), dim3(kp.nblocks),
                      dim3(kThreads), 0, st, kp);
   return hipGetLastError();
 }
 
+template <int CT, int BMODE, int MODE>
+hipError_t launch_grouped_or_dense(const KParams& kp, bool grouped, hipStream_t st) {
+  return grouped ? launch_t<CT, BMODE, MODE, true>(kp, st) : launch_t<CT, BMODE, MODE, false>(kp, st);
+}
+
 template <int CT, int BMODE>
-hipError_t launch_mode(const KParams& kp, bool nopromo, bool grouped, hipStream_t st) {
-  if (grouped) {
-    return nopromo ? launch_t<CT, BMODE, true, true>(kp, st) : launch_t<CT, BMODE, false, true>(kp, st);
+hipError_t launch_mode(const KParams& kp, int mode, bool grouped, hipStream_t st) {
+  switch (mode) {
+    case kModeExact: return launch_grouped_or_dense<CT, BMODE, kModeExact>(kp, grouped, st);
+    case kModeFp8: return launch_grouped_or_dense<CT, BMODE, kModeFp8>(kp, grouped, st);
+    default: return launch_grouped_or_dense<CT, BMODE, kModeFp8NoPromo>(kp, grouped, st);
   }
-  return nopromo ? launch_t<CT, BMODE, true, false>(kp, st) : launch_t<CT, BMODE, false, false>(kp, st);
 }
 
 }  // namespace
@@ -374,12 +556,15 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t nblocks = tiles_m * kp.tiles_n;
   if (nblocks == 0) return hipSuccess;
   kp.nblocks = (int)nblocks;
+  const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION) ? kModeFp8NoPromo
+                   : (g.flags & FP8FG_GEMM_FP8_MFMA)   ? kModeFp8
+                                                        : kModeExact;
   if (g.c_type == 0) {
-    return g.b_scale_mode == 0 ? launch_mode<0, 0>(kp, g.no_promotion, grouped, st)
-                               : launch_mode<0, 1>(kp, g.no_promotion, grouped, st);
+    return g.b_scale_mode == 0 ? launch_mode<0, 0>(kp, mode, grouped, st)
+                               : launch_mode<0, 1>(kp, mode, grouped, st);
   }
-  return g.b_scale_mode == 0 ? launch_mode<1, 0>(kp, g.no_promotion, grouped, st)
-                             : launch_mode<1, 1>(kp, g.no_promotion, grouped, st);
+  return g.b_scale_mode == 0 ? launch_mode<1, 0>(kp, mode, grouped, st)
+                             : launch_mode<1, 1>(kp, mode, grouped, st);
 }
 
 }  // namespace fp8fg

@@ -54,7 +54,7 @@ struct GemmArgs {
   void* c;
   int c_type;          // 0 bf16, 1 f32
   int64_t ldc;
-  bool no_promotion;
+  int flags;           // FP8FG_GEMM_* bit set
   // grouped
   int64_t G;           // 0 = dense
   const int32_t* offsets;

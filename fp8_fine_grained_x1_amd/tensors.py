@@ -65,26 +65,27 @@ def quantize_block(w, pow2=False, transpose=True, stream=None):
 
 
 def gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16, col_scales=False, no_promotion=False,
-         out=None, stream=None):
-    """col_scales=False: sb [K/128][N/128] block scales; True: sb [N][K/128]."""
+         fp8_mfma=False, out=None, stream=None):
+    """col_scales=False: sb [K/128][N/128] block scales; True: sb [N][K/128].
+    no_promotion: per-tensor scales (sa, sb hold one value each), whole-K
+    FP8 matrix-core accumulation.  fp8_mfma: K-group partial sums from the
+    FP8 MFMA instead of the exact default path."""
     M, K = qa.shape
     N = qb.shape[0]
     c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qa.device)
-    if col_scales:
-        sb_ns, sb_ks = sb.stride(0), sb.stride(1)
-        mode = B.FP8FG_BSCALE_COL
-    else:
-        sb_ns, sb_ks = sb.stride(1), sb.stride(0)
-        mode = B.FP8FG_BSCALE_BLOCK128
+    mode = B.FP8FG_BSCALE_COL if col_scales else B.FP8FG_BSCALE_BLOCK128
     if no_promotion:
         # per-tensor scales broadcast with zero strides
         sa_ms, sa_ks, sb_ns, sb_ks = 0, 0, 0, 0
     else:
         sa_ms, sa_ks = sa.stride(0), sa.stride(1)
+        if col_scales:
+            sb_ns, sb_ks = sb.stride(0), sb.stride(1)
+        else:
+            sb_ns, sb_ks = sb.stride(1), sb.stride(0)
+    flags = (B.FP8FG_GEMM_NO_PROMOTION if no_promotion else 0) | (B.FP8FG_GEMM_FP8_MFMA if fp8_mfma else 0)
     B.fp8_gemm_blockscaled(M, N, K, qa, qa.stride(0), sa, sa_ms, sa_ks, qb, qb.stride(0), sb,
-                           sb_ns, sb_ks, mode, c, _CTYPE[c.dtype], c.stride(0),
-                           B.FP8FG_GEMM_NO_PROMOTION if no_promotion else B.FP8FG_GEMM_DEFAULT,
-                           stream)
+                           sb_ns, sb_ks, mode, c, _CTYPE[c.dtype], c.stride(0), flags, stream)
     return c
 
 

@@ -137,6 +137,7 @@ def test_block_validation(lib, kw, status):
     (dict(b_scale_mode=3), B.FP8FG_EINVAL),
     (dict(c_type=B.FP8FG_E4M3), B.FP8FG_EINVAL),
     (dict(flags=4), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_FP8_MFMA, c=None), B.FP8FG_EINVAL),   # flag accepted, then null c
     (dict(M=-1), B.FP8FG_EINVAL),
     (dict(sa_ms=-2), B.FP8FG_EINVAL),
     (dict(flags=B.FP8FG_GEMM_NO_PROMOTION), B.FP8FG_EINVAL),   # per-K scales with no promotion

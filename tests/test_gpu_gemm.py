@@ -16,8 +16,8 @@ import oracle
 from fp8_fine_grained_x1_amd import binding as B
 from fp8_fine_grained_x1_amd import tensors as T
 from fp8_fine_grained_x1_amd import workloads
-from gpu_util import (DEV, bf16_dev, check_bf16_output, check_gemm, f32, f32_dev, host, say,
-                      workload)
+from gpu_util import (DEV, bf16_dev, check_bf16_output, check_gemm, f32, f32_dev, fp8_mfma_bound,
+                      host, say, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,8 @@ def test_column_scales(M, N, K):
 
 
 def test_no_promotion_per_tensor():
+    # the naive baseline: per-tensor scales, whole-K accumulation in the FP8
+    # matrix core.  Its error is bounded by the FP8 MFMA's 8-product groups.
     M, N, K = 128, 256, 1024
     a = rand_bits(M, K, seed=21, uniform=True)
     b = rand_bits(K, N, seed=22, uniform=True)
@@ -128,8 +130,31 @@ def test_no_promotion_per_tensor():
     qb = torch.from_numpy(np.ascontiguousarray(qbo.T)).to(DEV)
     sa = torch.tensor([s_a], dtype=torch.float32, device=DEV)
     sb = torch.tensor([s_b], dtype=torch.float32, device=DEV)
-    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, no_promotion=True))
-    check_gemm(c32, oracle.gemm_per_tensor(qao, s_a, qbo, s_b), "no-promotion")
+    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, no_promotion=True)).astype(np.float64)
+    ref = oracle.gemm_per_tensor(qao, s_a, qbo, s_b)
+    bound = fp8_mfma_bound(qao, s_a, qbo, s_b, promote=False)
+    err = np.abs(c32 - ref)
+    say("no-promotion: rel_frob=%.3e max_rel=%.3e; max err/bound=%.3f" % (
+        oracle.rel_frob(c32, ref), oracle.max_rel(c32, ref), np.max(err / bound)))
+    assert np.all(err <= bound)
+
+
+def test_fp8_mfma_flag_within_group_bound():
+    # promoted FP8-MFMA path: each K group's partial sum from the FP8 MFMA
+    M, N, K = 64, 256, 640
+    a = rand_bits(M, K, seed=23, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=24, std=0.02)
+    qa, sa = T.quantize_1x128(bf16_dev(a))
+    qb, sb = T.quantize_block(bf16_dev(b))
+    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, fp8_mfma=True)).astype(np.float64)
+    qao, sao = oracle.quantize_1x128(f32(a))
+    qbo, sbo = oracle.quantize_128x128(f32(b))
+    ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+    bound = fp8_mfma_bound(qao, sao, qbo, np.repeat(sbo, 128, axis=1))
+    err = np.abs(c32 - ref)
+    say("fp8-mfma promoted: rel_frob=%.3e max_rel=%.3e; max err/bound=%.3f" % (
+        oracle.rel_frob(c32, ref), oracle.max_rel(c32, ref), np.max(err / bound)))
+    assert np.all(err <= bound)
 
 
 # ---------------------------------------------------------------- grouped
