@@ -33,10 +33,11 @@
 //   * workgroup tile 128x128, four waves in a 2x2 arrangement, each wave a
 //     64x64 sub-tile;
 //   * A and B tiles (128 rows x 128 K bytes each) move HBM/L2 -> LDS with
-//     global_load_lds_dwordx4 (no VGPR staging), double-buffered so the next
-//     K group streams in while the current one is multiplied; the 16-byte
-//     chunks of each 128-byte row are XOR-swizzled by (row % 8) so that
-//     fragment reads of 8 consecutive rows hit distinct LDS banks;
+//     buffer_load_dwordx4 ... lds (no VGPR staging; the K offset rides in an
+//     SGPR), double-buffered so the next K group streams in while the current
+//     one is multiplied; the 16-byte chunks of each 128-byte row are
+//     XOR-swizzled by (row / 2) % 8 so that fragment reads of 16 consecutive
+//     rows hit distinct LDS banks;
 //   * per-row scales of A (and per-column scales of B in the column mode) are
 //     loaded into registers two K groups ahead and written into a separate
 //     LDS object one group ahead, so that neither ever waits for the tile
@@ -108,9 +109,21 @@ struct KParams {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
+// Buffer resource over [base, base + bytes) (gfx9 raw buffer, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// 16 bytes per lane from rsrc + voffset + soffset into lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
+                                      void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voffset, soffset, 0, 0);
+}
+// LDS tile layout: row r of a 128-byte-per-row tile keeps logical 16-byte
+// chunk c at physical chunk c ^ swz(r).  With 64 LDS banks a 16-byte read by
+// 16 consecutive lanes covers 16 consecutive rows; swz(r) = (r / 2) % 8 puts
+// them in 16 distinct bank groups (rows r and r + 1 differ in the upper/lower
+// half of the 256-byte bank window).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -224,56 +237,59 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
 
   // ---- per-lane copy sources.  Instruction i of wave w fills LDS rows
   // (4i + w) * 8 .. +8; lane l writes physical chunk l % 8 of row l / 8,
-  // which holds logical K chunk (l % 8) ^ (row % 8).
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
-  const uint8_t* a_src[4];
-  const uint8_t* b_src[4];
+  // which holds logical K chunk (l % 8) ^ swz(row).  Tile-relative byte
+  // offsets go in the VGPR offset, the K group's offset in the SGPR offset.
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kBN * p.ldb));
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (i * 4 + wave) * 8 + lrow;
+    const int r = (i * 4 + wave) * 8 + (lane >> 3);
     const int ra = r < rows_valid ? r : rows_valid - 1;  // ragged M: repeat the last row
-    a_src[i] = A + (row_base + ra) * p.lda + lchunk * 16;
-    b_src[i] = B + (n0 + r) * p.ldb + lchunk * 16;
+    const int lchunk = (lane & 7) ^ swz(r);
+    a_off[i] = (uint32_t)(ra * p.lda + lchunk * 16);
+    b_off[i] = (uint32_t)(r * p.ldb + lchunk * 16);
   }
-  // scales: lane l of wave 0 (A rows) / wave 1 (B columns) copies entries l, l + 64
-  const float* sa_src[2];
-  const float* sbc_src[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = h * 64 + lane;
-    const int ra = r < rows_valid ? r : rows_valid - 1;
-    sa_src[h] = p.sa + (row_base + ra) * p.sa_ms;
-    sbc_src[h] = SB + (n0 + r) * p.sb_ns;
+  // scales: lane l of wave 0 (A rows) / wave 1 (B columns in the per-column
+  // mode) copies entries l and l + 64 of the K group
+  const bool scale_wave = kPromote && (wave == 0 || (BMODE == 1 && wave == 1));
+  const float* sc_src0;
+  const float* sc_src1;
+  int64_t sc_ks;
+  if (wave == 0) {
+    const int r0 = lane < rows_valid ? lane : rows_valid - 1;
+    const int r1 = lane + 64 < rows_valid ? lane + 64 : rows_valid - 1;
+    sc_src0 = p.sa + (row_base + r0) * p.sa_ms;
+    sc_src1 = p.sa + (row_base + r1) * p.sa_ms;
+    sc_ks = p.sa_ks;
+  } else {
+    sc_src0 = SB + (n0 + lane) * p.sb_ns;
+    sc_src1 = SB + (n0 + lane + 64) * p.sb_ns;
+    sc_ks = p.sb_ks;
   }
 
   // Copies of K group kb's tiles into stage S (LDS DMA, no VGPRs).
   auto issue = [&](int kb, Stage& S) {
-    const int64_t koff = (int64_t)kb * kBK;
+    const uint32_t koff = (uint32_t)kb * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(a_src[i] + koff, S.a + (i * 4 + wave) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(a_rsrc, a_off[i], koff, S.a + (i * 4 + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_src[i] + koff, S.b + (i * 4 + wave) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(b_rsrc, b_off[i], koff, S.b + (i * 4 + wave) * 1024);
   };
   // Scales travel global -> VGPR -> LDS: loaded two K groups ahead (so the
   // wait at the top of the next group already covers them) and written into
   // their own LDS object at the end of the group before their use.
   auto load_scales = [&](int kb, float (&v)[2]) {
-    if (kPromote && wave == 0) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) v[h] = sa_src[h][(int64_t)kb * p.sa_ks];
-    } else if (kPromote && BMODE == 1 && wave == 1) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) v[h] = sbc_src[h][(int64_t)kb * p.sb_ks];
+    if (scale_wave) {
+      v[0] = sc_src0[(int64_t)kb * sc_ks];
+      v[1] = sc_src1[(int64_t)kb * sc_ks];
     }
   };
   auto store_scales = [&](Scales& SC, const float (&v)[2]) {
-    if (kPromote && wave == 0) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) SC.sa[h * 64 + lane] = v[h];
-    } else if (kPromote && BMODE == 1 && wave == 1) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) SC.sb[h * 64 + lane] = v[h];
+    if (scale_wave) {
+      float* dst = wave == 0 ? SC.sa : SC.sb;
+      dst[lane] = v[0];
+      dst[lane + 64] = v[1];
     }
   };
   float scr0[2] = {0.f, 0.f}, scr1[2] = {0.f, 0.f};  // scale registers, two sets
@@ -303,6 +319,25 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
                      float (&sc_store)[2], float (&sc_load)[2], float& sbv) {
       wait_vmcnt0();    // this wave's copies of K group kb have landed in LDS
       __syncthreads();  // ... and everyone's; the other stage is free again
+      // raw FP8 fragments, 16 bytes per lane and tile per chunk (= two
+      // 16-wide K steps); chunk c + 1 is read while chunk c is converted and
+      // multiplied, so the LDS latency hides behind the MFMAs.
+      uint4 ra[4][2], rb[4][2];
+      auto read_chunk = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = wm * 64 + i * 32 + lr;
+          ra[c][i] = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = wn * 64 + j * 32 + lr;
+          rb[c][j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
+        }
+      };
+      read_chunk(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // copies of the next K group, issued after this group's first reads
       float sbv_next = 0.f;
       if (kb + 1 < nkb) {
         if (BMODE == 0) sbv_next = sb_blk[(int64_t)(kb + 1) * p.sb_ks];
@@ -312,27 +347,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
       v16f P[2][2];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // raw FP8: 16 bytes per lane and tile = two 16-wide K steps
-        uint4 ra[2], rb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = wm * 64 + i * 32 + lr;
-          ra[i] = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((4 * g + c) ^ (row & 7)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = wn * 64 + j * 32 + lr;
-          rb[j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ (row & 7)) << 4));
-        }
+        if (c + 1 < 4) read_chunk(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           v8bf af[2], bf[2];
 #pragma unroll
           for (int i = 0; i < 2; ++i)
-            af[i] = h ? fp8x8_to_bf16(ra[i].z, ra[i].w) : fp8x8_to_bf16(ra[i].x, ra[i].y);
+            af[i] = h ? fp8x8_to_bf16(ra[c][i].z, ra[c][i].w) : fp8x8_to_bf16(ra[c][i].x, ra[c][i].y);
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            bf[j] = h ? fp8x8_to_bf16(rb[j].z, rb[j].w) : fp8x8_to_bf16(rb[j].x, rb[j].y);
+            bf[j] = h ? fp8x8_to_bf16(rb[c][j].z, rb[c][j].w) : fp8x8_to_bf16(rb[c][j].x, rb[c][j].y);
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -422,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 64 + i * 16 + fr;
-        const int sw = row & 7;
+        const int sw = swz(row);
         const uint4 lo = *reinterpret_cast<const uint4*>(S.a + row * 128 + ((fc ^ sw) << 4));
         const uint4 hi = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((fc + 1) ^ sw) << 4));
         af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -430,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = wn * 64 + j * 16 + fr;
-        const int sw = row & 7;
+        const int sw = swz(row);
         const uint4 lo = *reinterpret_cast<const uint4*>(S.b + row * 128 + ((fc ^ sw) << 4));
         const uint4 hi = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((fc + 1) ^ sw) << 4));
         bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
