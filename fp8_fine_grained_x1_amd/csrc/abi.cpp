@@ -111,6 +111,7 @@ int fp8_quantize_rowtile(const void* x, int x_type, int64_t rows, int64_t cols, 
     return FP8FG_EALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (tile == FP8FG_TILE_1x128) {
+    if (rows * (cols / 128) > (int64_t)1 << 31) return FP8FG_EUNSUPPORTED;
     fp8fg::RowtileArgs a{x, x_type, rows, cols, ldx, scale_rule, q, ldq, s, s_rs, s_ts};
     return launched(fp8fg::launch_quant_1x128(a, st));
   }

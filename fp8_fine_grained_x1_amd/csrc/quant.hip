@@ -15,8 +15,9 @@
 //   16-byte load for bf16), so a wave reads 4 consecutive tiles = 1 KiB of
 //   contiguous bf16.  The tile max is a 4-step DPP reduction inside a DPP
 //   row.  Each lane packs its 8 bytes with two v_cvt_pk_fp8_f32 pairs and
-//   writes them with one 8-byte store.  A grid-stride loop keeps 4 tiles per
-//   lane-group in flight.
+//   writes them with one 8-byte store.  A grid-stride loop keeps 2 tiles per
+//   lane-group in flight; the tile -> (row, tile column) split is a 32-bit
+//   multiply-high division.
 //
 // quant_tile128: one 256-thread workgroup per 128x128 block.  Thread
 //   (rg, cg) = (tid / 16, tid % 16) holds rows 8rg..8rg+7 x columns
@@ -24,8 +25,8 @@
 //   lanes (fully used 256-byte segments for bf16).  Column (128x1) or block
 //   maxima are reduced through LDS.  For the transposed layouts the bytes
 //   are converted directly in column order -- the conversion instruction
-//   takes any two registers -- so the transpose costs no extra ALU work;
-//   each lane then stores 8 contiguous bytes of an output row.
+//   takes any two registers -- and staged through LDS, so that each lane
+//   stores 16 contiguous bytes and a wave writes 8 whole 128-byte output rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,20 +39,21 @@ namespace {
 
 constexpr int kQThreads = 256;
 constexpr int kGroupsPerBlock = kQThreads / 16;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;
+constexpr int kTPitch = 144;  // LDS row pitch (bytes) of the transposing store
 
-// Position of a lane-group's current tile, stepped without division.
-struct TilePos {
-  int64_t r, tc;
+// n / d for 32-bit n by multiply-high and shift (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", PLDI 1994):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (umulhi(n, m) + n) >> l for every n < 2^32 (the sum is formed in
+// 64 bits).
+struct FastDiv {
+  uint32_t d, m, l;
 };
 
-__device__ __forceinline__ void step_pos(TilePos& p, int64_t dr, int64_t dtc, int64_t tpr) {
-  p.r += dr;
-  p.tc += dtc;
-  if (p.tc >= tpr) {
-    p.tc -= tpr;
-    p.r += 1;
-  }
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  const uint64_t t = (uint64_t)__umulhi(n, f.m) + n;
+  return (uint32_t)(t >> f.l);
 }
 
 template <int XT>
@@ -70,30 +72,30 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, f
   }
 }
 
+// Tiles are numbered row-major (t = r * tiles_per_row + tc); lane group g of
+// the grid handles tiles g, g + G, ... (G = number of lane groups), two per
+// iteration so that both loads are in flight before either is processed.
 template <int XT, int RULE>
 __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
-    const void* __restrict__ x, int64_t ntiles, int64_t tpr, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_rs, int64_t s_ts,
-    int64_t step_r, int64_t step_tc) {
+    const void* __restrict__ x, uint32_t ntiles, FastDiv tpr, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_rs, int64_t s_ts) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t group = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
-  const int64_t ngroups = (int64_t)gridDim.x * kGroupsPerBlock;
+  const uint32_t group = blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
+  const uint32_t ngroups = gridDim.x * kGroupsPerBlock;
 
-  TilePos pos{group / tpr, group % tpr};
-  for (int64_t t0 = group; t0 < ntiles; t0 += kUnroll * ngroups) {
+  for (uint32_t t0 = group; t0 < ntiles; t0 += kUnroll * ngroups) {
     float v[kUnroll][8];
-    TilePos p[kUnroll];
-    bool ok[kUnroll];
+    uint32_t r[kUnroll], tc[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      p[u] = pos;
-      ok[u] = (t0 + (int64_t)u * ngroups) < ntiles;
-      if (ok[u]) load8<XT>(x, p[u].r * ldx + p[u].tc * 128 + lane16 * 8, v[u]);
-      step_pos(pos, step_r, step_tc, tpr);
+      const uint32_t t = t0 + u * ngroups;
+      r[u] = fast_div(t, tpr);
+      tc[u] = t - r[u] * tpr.d;
+      if (t < ntiles) load8<XT>(x, (int64_t)r[u] * ldx + tc[u] * 128 + lane16 * 8, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (!ok[u]) continue;
+      if (t0 + u * ngroups >= ntiles) continue;
       float m = fabsf(v[u][0]);
 #pragma unroll
       for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
       uint2 out;
       out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
       out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
-      *reinterpret_cast<uint2*>(q + p[u].r * ldq + p[u].tc * 128 + lane16 * 8) = out;
-      if (lane16 == 0) s[p[u].r * s_rs + p[u].tc * s_ts] = sc.s;
+      *reinterpret_cast<uint2*>(q + (int64_t)r[u] * ldq + tc[u] * 128 + lane16 * 8) = out;
+      if (lane16 == 0) s[(int64_t)r[u] * s_rs + (int64_t)tc[u] * s_ts] = sc.s;
     }
   }
 }
@@ -205,12 +207,29 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
       v[i][j] = RULE == 0 ? div_by_scale(v[i][j], ss[j], ys[j]) : v[i][j] * ys[j];
 
   if constexpr (TRANSPOSE) {
+    // Output row c (an input column) is 128 contiguous bytes.  Stage the
+    // block through LDS so that every lane stores 16 bytes and a wave writes
+    // 8 whole rows: row pitch 144 bytes and 16-byte chunks XOR-swizzled by
+    // (c / 16) % 8 keep the scattered 8-byte writes and the row reads off
+    // the same LDS banks.
+    __shared__ __align__(16) uint8_t tbuf[128 * kTPitch];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint2 out;
       out.x = pack4_e4m3(v[0][j], v[1][j], v[2][j], v[3][j]);
       out.y = pack4_e4m3(v[4][j], v[5][j], v[6][j], v[7][j]);
-      *reinterpret_cast<uint2*>(q + (c0 + cg * 8 + j) * ldq + r0 + rg * 8) = out;
+      const int c = cg * 8 + j;
+      const int chunk = (rg >> 1) ^ ((c >> 4) & 7);
+      *reinterpret_cast<uint2*>(tbuf + c * kTPitch + chunk * 16 + (rg & 1) * 8) = out;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int k = it * kQThreads + tid;
+      const int c = k >> 3;
+      const int chunk = k & 7;
+      const uint4 w = *reinterpret_cast<const uint4*>(tbuf + c * kTPitch + ((chunk ^ ((c >> 4) & 7)) << 4));
+      *reinterpret_cast<uint4*>(q + (c0 + c) * ldq + r0 + chunk * 16) = w;
     }
   } else {
 #pragma unroll
@@ -223,17 +242,24 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
   }
 }
 
+FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+
 template <int XT, int RULE>
 hipError_t launch_1x128_t(const RowtileArgs& a, hipStream_t st) {
   const int64_t tpr = a.cols / 128;
   const int64_t ntiles = a.rows * tpr;
-  const int64_t want = (ntiles + kGroupsPerBlock * kUnroll - 1) / (kGroupsPerBlock * kUnroll);
-  const int64_t cap = (int64_t)device_cu_count() * 16;
+  const int64_t per_block = kGroupsPerBlock * kUnroll;
+  const int64_t want = (ntiles + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)device_cu_count() * 14;
   const int64_t blocks = want < cap ? want : cap;
-  const int64_t ngroups = blocks * kGroupsPerBlock;
   hipLaunchKernelGGL((quant_1x128_kernel<XT, RULE>), dim3((unsigned)blocks), dim3(kQThreads), 0, st,
-                     a.x, ntiles, tpr, a.ldx, a.q, a.ldq, a.s, a.s_rs, a.s_ts, ngroups / tpr,
-                     ngroups % tpr);
+                     a.x, (uint32_t)ntiles, make_fast_div((uint32_t)tpr), a.ldx, a.q, a.ldq, a.s,
+                     a.s_rs, a.s_ts);
   return hipGetLastError();
 }
 
