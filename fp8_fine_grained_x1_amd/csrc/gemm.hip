@@ -279,24 +279,28 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
   // Scales travel global -> VGPR -> LDS: loaded two K groups ahead (so the
   // wait at the top of the next group already covers them) and written into
   // their own LDS object at the end of the group before their use.
-  auto load_scales = [&](int kb, float (&v)[2]) {
+  // B block scales: one value per K group for this tile's 128 columns.
+  const float* sb_blk = SB + __builtin_amdgcn_readfirstlane((int)(n0 >> 7)) * p.sb_ns;
+  // In the block mode the B scale of the K group is folded in before the
+  // store (LDS then holds sa(m, kb) * sb(kb, n0 / 128)), so the promotion is
+  // a single FMA per element.
+  auto load_scales = [&](int kb, float (&v)[3]) {
     if (scale_wave) {
       v[0] = sc_src0[(int64_t)kb * sc_ks];
       v[1] = sc_src1[(int64_t)kb * sc_ks];
+      if (BMODE == 0) v[2] = sb_blk[(int64_t)kb * p.sb_ks];
     }
   };
-  auto store_scales = [&](Scales& SC, const float (&v)[2]) {
+  auto store_scales = [&](Scales& SC, const float (&v)[3]) {
     if (scale_wave) {
       float* dst = wave == 0 ? SC.sa : SC.sb;
-      dst[lane] = v[0];
-      dst[lane + 64] = v[1];
+      const float f = (BMODE == 0 && wave == 0) ? v[2] : 1.0f;
+      dst[lane] = v[0] * f;
+      dst[lane + 64] = v[1] * f;
     }
   };
-  float scr0[2] = {0.f, 0.f}, scr1[2] = {0.f, 0.f};  // scale registers, two sets
+  float scr0[3] = {0.f, 0.f, 0.f}, scr1[3] = {0.f, 0.f, 0.f};  // scale registers, two sets
 
-  // B block scales: one value per K group for this tile's 128 columns
-  // (wave-uniform), loaded one group ahead.
-  const float* sb_blk = SB + __builtin_amdgcn_readfirstlane((int)(n0 >> 7)) * p.sb_ns;
 
   if constexpr (MODE == kModeExact) {
     // ================================================================ BF16 MFMA
@@ -315,13 +319,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx, Scales& NS,
-                     float (&sc_store)[2], float (&sc_load)[2], float& sbv) {
+    // Pipeline inside a K group: the 16-byte chunk holding K steps 2c, 2c+1
+    // is read from LDS about two steps before its first use, and the BF16
+    // fragments of step s + 1 are converted while the 4 MFMAs of step s run
+    // (interleaved one MFMA : four conversions).
+    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx,
+                     float (&sc_store)[3], float (&sc_load)[3], Scales& NS) {
       wait_vmcnt0();    // this wave's copies of K group kb have landed in LDS
       __syncthreads();  // ... and everyone's; the other stage is free again
-      // raw FP8 fragments, 16 bytes per lane and tile per chunk (= two
-      // 16-wide K steps); chunk c + 1 is read while chunk c is converted and
-      // multiplied, so the LDS latency hides behind the MFMAs.
       uint4 ra[4][2], rb[4][2];
       auto read_chunk = [&](int c) {
 #pragma unroll
@@ -335,46 +340,53 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
           rb[c][j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
         }
       };
+      v8bf af[2][2], bf[2][2];  // [step parity][tile]
+      auto convert = [&](int st) {
+        const int c = st >> 1, h = st & 1, par = st & 1;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[par][i] = h ? fp8x8_to_bf16(ra[c][i].z, ra[c][i].w) : fp8x8_to_bf16(ra[c][i].x, ra[c][i].y);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bf[par][j] = h ? fp8x8_to_bf16(rb[c][j].z, rb[c][j].w) : fp8x8_to_bf16(rb[c][j].x, rb[c][j].y);
+      };
       read_chunk(0);
+      read_chunk(1);
       __builtin_amdgcn_sched_barrier(0);
       // copies of the next K group, issued after this group's first reads
-      float sbv_next = 0.f;
-      if (kb + 1 < nkb) {
-        if (BMODE == 0) sbv_next = sb_blk[(int64_t)(kb + 1) * p.sb_ks];
-        issue(kb + 1, Nx);
-      }
+      if (kb + 1 < nkb) issue(kb + 1, Nx);
       if (kb + 2 < nkb) load_scales(kb + 2, sc_load);
+      convert(0);
+      __builtin_amdgcn_sched_barrier(0);
       v16f P[2][2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c + 1 < 4) read_chunk(c + 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int st = 0; st < 8; ++st) {
+        const int par = st & 1;
+        if ((st & 1) && (st >> 1) + 2 < 4) read_chunk((st >> 1) + 2);
+        if (st + 1 < 8) convert(st + 1);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          v8bf af[2], bf[2];
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            af[i] = h ? fp8x8_to_bf16(ra[c][i].z, ra[c][i].w) : fp8x8_to_bf16(ra[c][i].x, ra[c][i].y);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            bf[j] = h ? fp8x8_to_bf16(rb[c][j].z, rb[c][j].w) : fp8x8_to_bf16(rb[c][j].x, rb[c][j].y);
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              if (c == 0 && h == 0) {
-                const v16f z = {};
-                P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], z, 0, 0, 0);
-              } else {
-                P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], P[i][j], 0, 0, 0);
-              }
+          for (int j = 0; j < 2; ++j) {
+            if (st == 0) {
+              const v16f z = {};
+              P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[par][i], bf[par][j], z, 0, 0, 0);
+            } else {
+              P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[par][i], bf[par][j], P[i][j], 0, 0, 0);
             }
+          }
+        if ((st & 1) && (st >> 1) + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (st + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // promotion: the row scales of this lane are tile i, rows 8 q + 4 g + t
+      // promotion: the scales of this lane's rows are tile i, rows 8 q + 4 g + t
       float sbc[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 32 + lr] : sbv;
+      for (int j = 0; j < 2; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 32 + lr] : 1.0f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -382,27 +394,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
           const float4 s4 = *reinterpret_cast<const float4*>(SS.sa + wm * 64 + i * 32 + 8 * q + 4 * g);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const float s[4] = {s4.x * sbc[j], s4.y * sbc[j], s4.z * sbc[j], s4.w * sbc[j]};
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t], s[t], acc[i][j][4 * q + t]);
+            for (int t = 0; t < 4; ++t) {
+              const float sc = BMODE == 1 ? sv[t] * sbc[j] : sv[t];
+              acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t], sc, acc[i][j][4 * q + t]);
+            }
           }
         }
       if (kb + 1 < nkb) store_scales(NS, sc_store);
-      sbv = sbv_next;
     };
 
-    float sbv = 0.f;
     if (nkb > 0) {
-      if (BMODE == 0) sbv = sb_blk[0];
       load_scales(0, scr0);
       if (nkb > 1) load_scales(1, scr1);
       store_scales(scales0, scr0);
       issue(0, stage0);
     }
     for (int kb = 0; kb < nkb; kb += 2) {
-      group(kb, stage0, scales0, stage1, scales1, scr1, scr0, sbv);
-      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scales0, scr0, scr1, sbv);
+      group(kb, stage0, scales0, stage1, scr1, scr0, scales1);
+      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scr0, scr1, scales0);
     }
 
     // ---- epilogue
@@ -433,15 +444,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
     const int fr = lane & 15;
     const int fc = (lane >> 4) * 2;
 
-    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx, Scales& NS,
-                     float (&sc_store)[2], float (&sc_load)[2], float& sbv) {
+    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx,
+                     float (&sc_store)[3], float (&sc_load)[3], Scales& NS) {
       wait_vmcnt0();
       __syncthreads();
-      float sbv_next = 0.f;
-      if (kb + 1 < nkb) {
-        if (kPromote && BMODE == 0) sbv_next = sb_blk[(int64_t)(kb + 1) * p.sb_ks];
-        issue(kb + 1, Nx);
-      }
+      if (kb + 1 < nkb) issue(kb + 1, Nx);
       if (kb + 2 < nkb) load_scales(kb + 2, sc_load);
       v8i af[4], bf[4];
 #pragma unroll
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
           sar[i][0] = t.x; sar[i][1] = t.y; sar[i][2] = t.z; sar[i][3] = t.w;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 16 + fr] : sbv;
+        for (int j = 0; j < 4; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 16 + fr] : 1.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -490,20 +497,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
         }
       }
       if (kb + 1 < nkb) store_scales(NS, sc_store);
-      sbv = sbv_next;
     };
 
-    float sbv = 0.f;
     if (nkb > 0) {
-      if (kPromote && BMODE == 0) sbv = sb_blk[0];
       load_scales(0, scr0);
       if (nkb > 1) load_scales(1, scr1);
       store_scales(scales0, scr0);
       issue(0, stage0);
     }
     for (int kb = 0; kb < nkb; kb += 2) {
-      group(kb, stage0, scales0, stage1, scales1, scr1, scr0, sbv);
-      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scales0, scr0, scr1, sbv);
+      group(kb, stage0, scales0, stage1, scr1, scr0, scales1);
+      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scr0, scr1, scales0);
     }
 
     // ---- epilogue
