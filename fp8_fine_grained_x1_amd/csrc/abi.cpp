@@ -48,6 +48,11 @@ constexpr int64_t kMaxGridY = 65535;
 
 namespace {
 
+constexpr int64_t kMaxPitchA = (int64_t)1 << 23;          // bytes per row of A
+constexpr int64_t kMaxPitchB = (int64_t)1 << 24;          // bytes per row of B
+constexpr int64_t kMaxScaleRowStride = (int64_t)1 << 21;  // elements
+constexpr int64_t kMaxScaleKSpan = (int64_t)1 << 29;      // elements
+
 int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                       const float* sa, int64_t sa_ms, int64_t sa_ks, const uint8_t* b,
                       int64_t ldb, const float* sb, int64_t sb_ns, int64_t sb_ks,
@@ -65,6 +70,16 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
   if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 || ldb % 16 ||
       !aligned(c, c_type == FP8FG_F32 ? 4 : 2) || !aligned(sa, 4) || !aligned(sb, 4))
     return FP8FG_EALIGN;
+  // The kernels address a tile's operands and scales with 32-bit buffer
+  // offsets (row pitch times tile rows, K offsets, scale strides).
+  const int64_t nkb = K / 128;
+  if (lda >= kMaxPitchA || ldb >= kMaxPitchB || K >= ((int64_t)1 << 31)) return FP8FG_EUNSUPPORTED;
+  if (!(flags & FP8FG_GEMM_NO_PROMOTION)) {
+    const int64_t kspan = kMaxScaleKSpan / (nkb > 0 ? nkb : 1);
+    if (sa_ms >= kMaxScaleRowStride || sa_ks >= kspan || sb_ks >= kspan)
+      return FP8FG_EUNSUPPORTED;
+    if (b_scale_mode == FP8FG_BSCALE_COL && sb_ns >= kMaxScaleRowStride) return FP8FG_EUNSUPPORTED;
+  }
   return FP8FG_OK;
 }
 
@@ -151,7 +166,8 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
   const int rc = check_gemm_common(M, N, K, a, lda, sa, sa_ms, sa_ks, b, ldb, sb, sb_ns, sb_ks,
                                    b_scale_mode, c, c_type, ldc, flags);
   if (rc != FP8FG_OK || M == 0 || N == 0) return rc;
-  if (((M + 127) / 128) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
+  const int64_t tm = fp8fg::gemm_tile_m();
+  if (((M + tm - 1) / tm) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
   fp8fg::GemmArgs g{M,  N,  K,  a,      lda,    sa, sa_ms,
                     sa_ks, b, ldb, sb, sb_ns, sb_ks, b_scale_mode,
                     c,  c_type, ldc, flags,
@@ -174,7 +190,8 @@ int fp8_grouped_gemm_blockscaled(int64_t G, const int32_t* offsets, int64_t M_to
   if (!offsets) return FP8FG_EINVAL;
   if (!aligned(offsets, 4)) return FP8FG_EALIGN;
   if (b_gs % 16) return FP8FG_EALIGN;
-  if (((M_total + 127) / 128 + G) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
+  const int64_t tm = fp8fg::gemm_tile_m();
+  if (((M_total + tm - 1) / tm + G) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
   fp8fg::GemmArgs g{M_total, N,  K,  a,      lda,    sa, sa_ms,
                     sa_ks,   b,  ldb, sb, sb_ns, sb_ks, FP8FG_BSCALE_BLOCK128,
                     c,       c_type, ldc, flags,

@@ -30,21 +30,24 @@
 //   applies per-tensor scales once -- the naive baseline.
 //
 // Shared structure:
-//   * workgroup tile 128x128, four waves in a 2x2 arrangement, each wave a
-//     64x64 sub-tile;
-//   * A and B tiles (128 rows x 128 K bytes each) move HBM/L2 -> LDS with
-//     buffer_load_dwordx4 ... lds (no VGPR staging; the K offset rides in an
-//     SGPR), double-buffered so the next K group streams in while the current
-//     one is multiplied; the 16-byte chunks of each 128-byte row are
-//     XOR-swizzled by (row / 2) % 8 so that fragment reads of 16 consecutive
-//     rows hit distinct LDS banks;
-//   * per-row scales of A (and per-column scales of B in the column mode) are
-//     loaded into registers two K groups ahead and written into a separate
-//     LDS object one group ahead, so that neither ever waits for the tile
-//     copies in flight; a B block scale is one wave-uniform load per K group,
-//     issued a group ahead;
+//   * workgroup tile 256 (M) x 128 (N), eight waves in a 4x2 arrangement,
+//     each wave a 64x64 sub-tile; one workgroup per CU;
+//   * A and B tiles (256 + 128 rows x 128 K bytes = 48 KB per K group) move
+//     HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging; the K
+//     offset rides in an SGPR) through three LDS stages, so the copies of
+//     K group kb + 2 stream in while kb is multiplied; the wait at the top of
+//     a group leaves the newest group's copies in flight (vmcnt = copies per
+//     group); the 16-byte chunks of each 128-byte row are XOR-swizzled by
+//     (row / 2) % 8 so that fragment reads of 16 consecutive rows hit
+//     distinct LDS banks;
+//   * the MFMA operands are passed B-first, so the accumulator of a lane
+//     holds one output row (and 4-element runs of columns): the row scale of
+//     A is then one value per lane and MFMA tile, loaded straight from
+//     global memory into registers two K groups ahead; a B block scale is one
+//     value per K group (all lanes load it); per-column B scales go through a
+//     small per-wave LDS array;
 //   * workgroup ids are remapped so that consecutive tiles run on the same
-//     XCD (each XCD has its own L2), and tiles are ordered in groups of 8
+//     XCD (each XCD has its own L2), and tiles are ordered in groups of
 //     M-tiles so that co-resident workgroups share A and B panels.
 // Grouped GEMM: the same tile kernel; a workgroup's linear tile id is
 // resolved against the device-side expert offsets (expert-major order), so
@@ -66,12 +69,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;
+constexpr int kBM = 256;
 constexpr int kBN = 128;
 constexpr int kBK = 128;
-constexpr int kThreads = 256;
-constexpr int kGroupM = 8;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupM = 4;
 constexpr int kE8M0One = 127;  // E8M0 encoding of 2^0
+// One buffer_load ... lds of a wave moves 64 lanes x 16 B = 8 rows of 128 B.
+constexpr int kDmaA = kBM / (8 * kWaves);  // per thread and K group
+constexpr int kDmaB = kBN / (8 * kWaves);
+constexpr int kDmaPerGroup = kDmaA + kDmaB;
 
 constexpr int kModeExact = 0;     // BF16 MFMA partial sums
 constexpr int kModeFp8 = 1;       // FP8 MFMA partial sums, promoted
@@ -80,11 +88,10 @@ constexpr int kModeFp8NoPromo = 2;
 struct __align__(16) Stage {
   uint8_t a[kBM * kBK];
   uint8_t b[kBN * kBK];
-};
-// Scales of one K group (A rows; B columns in the per-column mode).
-struct __align__(16) Scales {
-  float sa[kBM];
-  float sb[kBN];
+  // per-column B scales of the stage's K group, one copy per wave (columns
+  // wn*64 .. +64); filled by the same LDS copies as the tiles, so that reads
+  // of it wait only for this stage's copies
+  float colsc[kWaves][64];
 };
 
 struct KParams {
@@ -104,10 +111,10 @@ struct KParams {
   int G;
   int tiles_n;
   int nblocks;
+  int vec_store;  // c rows allow 4-element vector stores
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 // Buffer resource over [base, base + bytes) (gfx9 raw buffer, stride 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -118,6 +125,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset
                                       void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voffset, soffset, 0, 0);
 }
+// 4 bytes per lane into lds + 4 * lane.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
+                                     void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voffset, (int)soffset, 0));
+}
 // LDS tile layout: row r of a 128-byte-per-row tile keeps logical 16-byte
 // chunk c at physical chunk c ^ swz(r).  With 64 LDS banks a 16-byte read by
 // 16 consecutive lanes covers 16 consecutive rows; swz(r) = (r / 2) % 8 puts
@@ -125,8 +140,24 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset
 // half of the 256-byte bank window).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima; gfx9 splits
+// vmcnt over bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without a memory fence: __syncthreads() would also wait
+// for every copy in flight (vmcnt(0)).  Each wave has already waited for
+// the copies the next group reads (explicit vmcnt above), and LDS reads of
+// the stage about to be refilled completed before their MFMAs; the empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
 // that each XCD receives a contiguous range of logical tile ids.
@@ -147,18 +178,35 @@ __device__ __forceinline__ void grouped_order(int id, int tiles_m, int tiles_n, 
   tn = in / gm;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Round to nearest even (hardware conversion; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
 template <int CT>
 __device__ __forceinline__ void store_c(void* c, int64_t idx, float v) {
   if constexpr (CT == 0) {
-    reinterpret_cast<uint16_t*>(c)[idx] = f32_to_bf16_rne(v);
+    reinterpret_cast<uint16_t*>(c)[idx] = f32_to_bf16(v);
   } else {
     reinterpret_cast<float*>(c)[idx] = v;
+  }
+}
+// Four consecutive outputs c[idx .. idx + 3]; one 8-byte (bf16) or 16-byte
+// (f32) store when the row layout allows it.
+template <int CT>
+__device__ __forceinline__ void store_c4(void* c, int64_t idx, const float (&v)[4], bool vec) {
+  if (vec) {
+    if constexpr (CT == 0) {
+      uint2 u;
+      u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + idx) = u;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) store_c<CT>(c, idx + t, v[t]);
   }
 }
 
@@ -176,16 +224,20 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 template <int CT, int BMODE, int MODE, bool GROUPED>
-__global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p) {
   constexpr bool kPromote = MODE != kModeFp8NoPromo;
-  // Two stages of tiles and two of scales, each its own LDS object: with the
-  // K loop unrolled by two every access names its object at compile time, so
-  // the compiler can tell copies in flight into one stage from reads of the
-  // other and inserts no wait between them.
+  constexpr int kT = MODE == kModeExact ? 32 : 16;  // MFMA tile edge
+  constexpr int kTiles = 64 / kT;                   // MFMA tiles per wave along M (and N)
+  // Three stages of tiles, each its own LDS object: with the K loop unrolled
+  // by three every access names its object at compile time, so the compiler
+  // can tell copies in flight into one stage from reads of another and
+  // inserts no wait between them.
   __shared__ Stage stage0;
   __shared__ Stage stage1;
-  __shared__ Scales scales0;
-  __shared__ Scales scales1;
+  __shared__ Stage stage2;
+  constexpr bool kColDma = kPromote && BMODE == 1;  // column scales travel with the tiles
+  constexpr int kVmemWait = kDmaPerGroup + (kColDma ? 1 : 0);
+  static_assert(kDmaPerGroup <= 8, "one tile copy per K step");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -236,79 +288,121 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
   const int nkb = (int)(p.K / kBK);
 
   // ---- per-lane copy sources.  Instruction i of wave w fills LDS rows
-  // (4i + w) * 8 .. +8; lane l writes physical chunk l % 8 of row l / 8,
+  // (8i + w) * 8 .. +8; lane l writes physical chunk l % 8 of row l / 8,
   // which holds logical K chunk (l % 8) ^ swz(row).  Tile-relative byte
   // offsets go in the VGPR offset, the K group's offset in the SGPR offset.
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kBN * p.ldb));
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[kDmaA], b_off[kDmaB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (i * 4 + wave) * 8 + (lane >> 3);
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
     const int ra = r < rows_valid ? r : rows_valid - 1;  // ragged M: repeat the last row
-    const int lchunk = (lane & 7) ^ swz(r);
-    a_off[i] = (uint32_t)(ra * p.lda + lchunk * 16);
-    b_off[i] = (uint32_t)(r * p.ldb + lchunk * 16);
+    a_off[i] = (uint32_t)(ra * p.lda + (((lane & 7) ^ swz(r)) << 4));
   }
-  // scales: lane l of wave 0 (A rows) / wave 1 (B columns in the per-column
-  // mode) copies entries l and l + 64 of the K group
-  const bool scale_wave = kPromote && (wave == 0 || (BMODE == 1 && wave == 1));
-  const float* sc_src0;
-  const float* sc_src1;
-  int64_t sc_ks;
-  if (wave == 0) {
-    const int r0 = lane < rows_valid ? lane : rows_valid - 1;
-    const int r1 = lane + 64 < rows_valid ? lane + 64 : rows_valid - 1;
-    sc_src0 = p.sa + (row_base + r0) * p.sa_ms;
-    sc_src1 = p.sa + (row_base + r1) * p.sa_ms;
-    sc_ks = p.sa_ks;
-  } else {
-    sc_src0 = SB + (n0 + lane) * p.sb_ns;
-    sc_src1 = SB + (n0 + lane + 64) * p.sb_ns;
-    sc_ks = p.sb_ks;
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    b_off[i] = (uint32_t)(r * p.ldb + (((lane & 7) ^ swz(r)) << 4));
   }
+  // ---- scale sources (buffer loads: 32-bit offsets, checked on the host).
+  // A: this lane's output row in MFMA tile i is wm*64 + i*kT + lane % kT.
+  const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(p.sa + row_base * p.sa_ms, 0xFFFFFFFFu);
+  uint32_t sa_off[kTiles];
+#pragma unroll
+  for (int i = 0; i < kTiles; ++i) {
+    const int r = wm * 64 + i * kT + (lane & (kT - 1));
+    sa_off[i] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * p.sa_ms * 4);
+  }
+  // B: block mode, the scale of this tile's 128 columns (same for all
+  // lanes, into a register); per-column mode, column wn*64 + lane (copied
+  // into the stage's per-wave column-scale array).
+  const __amdgpu_buffer_rsrc_t sb_rsrc =
+      make_rsrc(SB + (BMODE == 0 ? (n0 >> 7) : n0) * p.sb_ns, 0xFFFFFFFFu);
+  const uint32_t sb_off = BMODE == 0 ? 0u : (uint32_t)((wn * 64 + lane) * p.sb_ns * 4);
 
-  // Copies of K group kb's tiles into stage S (LDS DMA, no VGPRs).
+
+  // A resource of size 0: loads through it fetch nothing and return zeros.
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(p.a, 0u);
+  // Copies of K group kb's tiles (and per-column B scales) into stage S (LDS
+  // DMA, no VGPRs).  Every group issues the same number of copies, so that
+  // the wait counts hold on every path; past the last K group they go
+  // through the empty resource (zeros into a stage that is not read again).
+  // Copy number `idx` (0 .. kVmemWait - 1) of K group kb; the copies of one
+  // group are spread over its K steps so that the address queues never fill
+  // and no wave stalls at issue.
+  auto issue_one = [&](int kb, Stage& S, int idx) {
+    const bool live = kb < nkb;
+    const uint32_t koff = live ? (uint32_t)kb * kBK : 0u;
+    if (idx < kDmaA) {
+      dma16(live ? a_rsrc : null_rsrc, a_off[idx], koff, S.a + (idx * kWaves + wave) * 1024);
+    } else if (idx < kDmaPerGroup) {
+      const int i = idx - kDmaA;
+      dma16(live ? b_rsrc : null_rsrc, b_off[i], koff, S.b + (i * kWaves + wave) * 1024);
+    } else if constexpr (kColDma) {
+      dma4(live ? sb_rsrc : null_rsrc, sb_off, live ? (uint32_t)(kb * p.sb_ks * 4) : 0u, &S.colsc[wave][0]);
+    }
+  };
   auto issue = [&](int kb, Stage& S) {
-    const uint32_t koff = (uint32_t)kb * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(a_rsrc, a_off[i], koff, S.a + (i * 4 + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_rsrc, b_off[i], koff, S.b + (i * 4 + wave) * 1024);
+    for (int i = 0; i < kVmemWait; ++i) issue_one(kb, S, i);
   };
-  // Scales travel global -> VGPR -> LDS: loaded two K groups ahead (so the
-  // wait at the top of the next group already covers them) and written into
-  // their own LDS object at the end of the group before their use.
-  // B block scales: one value per K group for this tile's 128 columns.
-  const float* sb_blk = SB + __builtin_amdgcn_readfirstlane((int)(n0 >> 7)) * p.sb_ns;
-  // In the block mode the B scale of the K group is folded in before the
-  // store (LDS then holds sa(m, kb) * sb(kb, n0 / 128)), so the promotion is
-  // a single FMA per element.
-  auto load_scales = [&](int kb, float (&v)[3]) {
-    if (scale_wave) {
-      v[0] = sc_src0[(int64_t)kb * sc_ks];
-      v[1] = sc_src1[(int64_t)kb * sc_ks];
-      if (BMODE == 0) v[2] = sb_blk[(int64_t)kb * p.sb_ks];
+  // Row scales of A (and the B block scale) of group kb into registers.
+  struct ScaleRegs {
+    float sa[kTiles];
+    float sb;
+  };
+  auto load_scales = [&](int kb, ScaleRegs& s) {
+    if constexpr (kPromote) {
+      const bool live = kb < nkb;
+      const __amdgpu_buffer_rsrc_t ra = live ? sa_rsrc : null_rsrc;
+      const uint32_t ka = live ? (uint32_t)(kb * p.sa_ks * 4) : 0u;
+#pragma unroll
+      for (int i = 0; i < kTiles; ++i) s.sa[i] = load_f32(ra, sa_off[i], ka);
+      if constexpr (BMODE == 0)
+        s.sb = load_f32(live ? sb_rsrc : null_rsrc, 0u, live ? (uint32_t)(kb * p.sb_ks * 4) : 0u);
     }
   };
-  auto store_scales = [&](Scales& SC, const float (&v)[3]) {
-    if (scale_wave) {
-      float* dst = wave == 0 ? SC.sa : SC.sb;
-      const float f = (BMODE == 0 && wave == 0) ? v[2] : 1.0f;
-      dst[lane] = v[0] * f;
-      dst[lane + 64] = v[1] * f;
-    }
+  // Top of K group kb: its copies (and every older memory load) have
+  // landed, for this wave and -- after the barrier -- for all; the stage
+  // read in group kb - 1 is free again.  Only the copies of group kb + 1
+  // (real or empty) may still be in flight.
+  auto wait_group = [&]() {
+    wait_vmcnt<kVmemWait>();
+    block_barrier();
   };
-  float scr0[3] = {0.f, 0.f, 0.f}, scr1[3] = {0.f, 0.f, 0.f};  // scale registers, two sets
 
+  ScaleRegs sr0{}, sr1{}, sr2{};
+  load_scales(0, sr0);
+  issue(0, stage0);
+  load_scales(1, sr1);
+  issue(1, stage1);
+  // The K loop: full triples of groups, then the remaining one or two.  No
+  // group is conditional inside the loop, so on every control-flow path the
+  // copies into the stage a group reads are followed by exactly one group's
+  // copies, and the compiler's own wait analysis agrees with wait_group.
+  auto k_loop = [&](auto& group) {
+    int kb = 0;
+    for (; kb + 3 <= nkb; kb += 3) {
+      group(kb, stage0, sr0, stage2, sr2);
+      group(kb + 1, stage1, sr1, stage0, sr0);
+      group(kb + 2, stage2, sr2, stage1, sr1);
+    }
+    const int rem = nkb - kb;
+    if (rem >= 1) {
+      group(kb, stage0, sr0, stage2, sr2);
+      if (rem == 2) group(kb + 1, stage1, sr1, stage0, sr0);
+    }
+  };
 
   if constexpr (MODE == kModeExact) {
     // ================================================================ BF16 MFMA
-    // Wave tile 64x64 = 2x2 tiles of 32x32.  Lane l serves row/column l % 32
-    // of a tile; lane group g = l / 32 takes K bytes [64 g, 64 g + 64) of each
-    // K group, 8 per 16-wide K step (the same permutation of K for A and B).
-    // Accumulator layout of v_mfma_f32_32x32x16_bf16: element r of lane l is
-    // row 8 (r / 4) + 4 g + r % 4, column l % 32.
+    // Wave tile 64x64 = 2x2 tiles of 32x32.  Lane l reads row l % 32 of an A
+    // tile and of a B tile; lane group g = l / 32 takes K bytes
+    // [64 g, 64 g + 64) of each K group, 8 per 16-wide K step (the same
+    // permutation of K for A and B).  With B as the first MFMA operand the
+    // accumulator element r of lane l is output row l % 32 and column
+    // 8 (r / 4) + 4 g + r % 4 of the tile.
     const int g = lane >> 5;
     const int lr = lane & 31;
     v16f acc[2][2];
@@ -323,10 +417,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
     // is read from LDS about two steps before its first use, and the BF16
     // fragments of step s + 1 are converted while the 4 MFMAs of step s run
     // (interleaved one MFMA : four conversions).
-    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx,
-                     float (&sc_store)[3], float (&sc_load)[3], Scales& NS) {
-      wait_vmcnt0();    // this wave's copies of K group kb have landed in LDS
-      __syncthreads();  // ... and everyone's; the other stage is free again
+    auto group = [&](int kb, const Stage& S, const ScaleRegs& sr, Stage& Nx, ScaleRegs& nsr) {
+      wait_group();
       uint4 ra[4][2], rb[4][2];
       auto read_chunk = [&](int c) {
 #pragma unroll
@@ -353,9 +445,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
       read_chunk(0);
       read_chunk(1);
       __builtin_amdgcn_sched_barrier(0);
-      // copies of the next K group, issued after this group's first reads
-      if (kb + 1 < nkb) issue(kb + 1, Nx);
-      if (kb + 2 < nkb) load_scales(kb + 2, sc_load);
+      // scales of K group kb + 2, after this group's first reads; its tile
+      // copies follow one per K step below
+      load_scales(kb + 2, nsr);
+      if constexpr (kColDma) issue_one(kb + 2, Nx, kDmaPerGroup);
       convert(0);
       __builtin_amdgcn_sched_barrier(0);
       v16f P[2][2];
@@ -370,71 +463,72 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
           for (int j = 0; j < 2; ++j) {
             if (st == 0) {
               const v16f z = {};
-              P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[par][i], bf[par][j], z, 0, 0, 0);
+              P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[par][j], af[par][i], z, 0, 0, 0);
             } else {
-              P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[par][i], bf[par][j], P[i][j], 0, 0, 0);
+              P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[par][j], af[par][i], P[i][j], 0, 0, 0);
             }
           }
+        if (st < kDmaPerGroup) issue_one(kb + 2, Nx, st);
         if ((st & 1) && (st >> 1) + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (st + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          if (m == 0 && st < kDmaPerGroup) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // promotion: the scales of this lane's rows are tile i, rows 8 q + 4 g + t
-      float sbc[2];
+      // promotion: tile i's row scale is one value per lane
+      if constexpr (BMODE == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 32 + lr] : 1.0f;
+        for (int i = 0; i < 2; ++i) {
+          const float s = sr.sa[i] * sr.sb;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 s4 = *reinterpret_cast<const float4*>(SS.sa + wm * 64 + i * 32 + 8 * q + 4 * g);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float sc = BMODE == 1 ? sv[t] * sbc[j] : sv[t];
-              acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t], sc, acc[i][j][4 * q + t]);
-            }
-          }
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[i][j][r], s, acc[i][j][r]);
         }
-      if (kb + 1 < nkb) store_scales(NS, sc_store);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 c4 = *reinterpret_cast<const float4*>(&S.colsc[wave][j * 32 + 8 * q + 4 * g]);
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t], sr.sa[i] * cv[t], acc[i][j][4 * q + t]);
+          }
+      }
     };
 
-    if (nkb > 0) {
-      load_scales(0, scr0);
-      if (nkb > 1) load_scales(1, scr1);
-      store_scales(scales0, scr0);
-      issue(0, stage0);
-    }
-    for (int kb = 0; kb < nkb; kb += 2) {
-      group(kb, stage0, scales0, stage1, scr1, scr0, scales1);
-      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scr0, scr1, scales0);
-    }
+    k_loop(group);
+    wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
 
-    // ---- epilogue
+    // ---- epilogue: lane holds row lr of tile i, columns 8q + 4g .. +3 of tile j
+    const bool vec = p.vec_store != 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + lr;
+      if (row >= rows_valid) continue;
+      const int64_t grow = row_base + row;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row >= rows_valid) continue;
-        const int64_t grow = row_base + row;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t col = n0 + wn * 64 + j * 32 + lr;
-          store_c<CT>(p.c, grow * p.ldc + col, acc[i][j][r]);
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = n0 + wn * 64 + j * 32 + 8 * q + 4 * g;
+          const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
         }
-      }
+    }
   } else {
     // ================================================================ FP8 MFMA
     // Wave tile 64x64 = 4x4 tiles of 16x16.  Lane l supplies row l % 16 and K
-    // bytes [32 (l/16), +32) of a K group; accumulator element r of lane l is
-    // row 4 (l/16) + r, column l % 16.
+    // bytes [32 (l/16), +32) of a K group; with B as the first operand the
+    // accumulator element r of lane l is output row l % 16, column
+    // 4 (l/16) + r of the tile.
     v4f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -444,12 +538,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
     const int fr = lane & 15;
     const int fc = (lane >> 4) * 2;
 
-    auto group = [&](int kb, const Stage& S, const Scales& SS, Stage& Nx,
-                     float (&sc_store)[3], float (&sc_load)[3], Scales& NS) {
-      wait_vmcnt0();
-      __syncthreads();
-      if (kb + 1 < nkb) issue(kb + 1, Nx);
-      if (kb + 2 < nkb) load_scales(kb + 2, sc_load);
+    auto group = [&](int kb, const Stage& S, const ScaleRegs& sr, Stage& Nx, ScaleRegs& nsr) {
+      wait_group();
       v8i af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -467,69 +557,76 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_blockscaled_kernel(KParams p
         const uint4 hi = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((fc + 1) ^ sw) << 4));
         bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
+      float cv[4][4];
+      if constexpr (kColDma) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 t = *reinterpret_cast<const float4*>(&S.colsc[wave][j * 16 + 4 * (lane >> 4)]);
+          cv[j][0] = t.x; cv[j][1] = t.y; cv[j][2] = t.z; cv[j][3] = t.w;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // scales and copies of K group kb + 2, issued after this group's reads
+      // (tile copies spread over the MFMAs, one every other one)
+      load_scales(kb + 2, nsr);
+      if constexpr (kColDma) issue_one(kb + 2, Nx, kDmaPerGroup);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (!kPromote) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            if ((j * 4 + i) % 2 == 0 && (j * 4 + i) / 2 < kDmaPerGroup) issue_one(kb + 2, Nx, (j * 4 + i) / 2);
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[i], bf[j], acc[i][j], 0, 0, 0, kE8M0One, 0, kE8M0One);
+                bf[j], af[i], acc[i][j], 0, 0, 0, kE8M0One, 0, kE8M0One);
+          }
       } else {
-        float sar[4][4];
-        float sbc[4];
+        if constexpr (!kColDma) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 t = *reinterpret_cast<const float4*>(SS.sa + wm * 64 + i * 16 + 4 * (lane >> 4));
-          sar[i][0] = t.x; sar[i][1] = t.y; sar[i][2] = t.z; sar[i][3] = t.w;
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cv[j][r] = sr.sb;
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sbc[j] = BMODE == 1 ? SS.sb[wn * 64 + j * 16 + fr] : 1.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            if ((j * 4 + i) % 2 == 0 && (j * 4 + i) / 2 < kDmaPerGroup) issue_one(kb + 2, Nx, (j * 4 + i) / 2);
             const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[i], bf[j], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+                bf[j], af[i], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              acc[i][j][r] = __builtin_fmaf(P[r], sar[i][r] * sbc[j], acc[i][j][r]);
+              acc[i][j][r] = __builtin_fmaf(P[r], sr.sa[i] * cv[j][r], acc[i][j][r]);
           }
         }
       }
-      if (kb + 1 < nkb) store_scales(NS, sc_store);
     };
 
-    if (nkb > 0) {
-      load_scales(0, scr0);
-      if (nkb > 1) load_scales(1, scr1);
-      store_scales(scales0, scr0);
-      issue(0, stage0);
-    }
-    for (int kb = 0; kb < nkb; kb += 2) {
-      group(kb, stage0, scales0, stage1, scr1, scr0, scales1);
-      if (kb + 1 < nkb) group(kb + 1, stage1, scales1, stage0, scr0, scr1, scales0);
-    }
+    k_loop(group);
+    wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
 
-    // ---- epilogue
+    // ---- epilogue: lane holds row fr of tile i, columns 4 (l/16) .. +3 of tile j
+    const bool vec = p.vec_store != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int row = wm * 64 + i * 16 + fr;
+      if (row >= rows_valid) continue;
+      const int64_t grow = row_base + row;
+      float rs = 1.0f;
+      if constexpr (!kPromote) rs = p.sa[grow * p.sa_ms];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (row >= rows_valid) continue;
-        const int64_t grow = row_base + row;
-        float rs = 1.0f;
-        if constexpr (!kPromote) rs = p.sa[grow * p.sa_ms];
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+        float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
-          float v = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][j][r];
           if constexpr (!kPromote) {
-            const float cs = BMODE == 0 ? sb_blk[0] : SB[col * p.sb_ns];
-            v = v * (rs * cs);
+            const float cs = BMODE == 0 ? SB[(n0 >> 7) * p.sb_ns] : SB[(col + r) * p.sb_ns];
+            v[r] = v[r] * (rs * cs);
           }
-          store_c<CT>(p.c, grow * p.ldc + col, v);
         }
+        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
       }
     }
   }
@@ -558,6 +655,8 @@ hipError_t launch_mode(const KParams& kp, int mode, bool grouped, hipStream_t st
 
 }  // namespace
 
+int64_t gemm_tile_m() { return kBM; }
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   KParams kp;
   kp.M = g.M;
@@ -580,6 +679,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   kp.sb_gs = g.sb_gs;
   kp.G = (int)g.G;
   kp.tiles_n = (int)(g.N / kBN);
+  const int esize = g.c_type == 0 ? 2 : 4;
+  kp.vec_store = (reinterpret_cast<uintptr_t>(g.c) % (4 * esize) == 0) && (g.ldc % 4 == 0);
   const bool grouped = g.G > 0;
   const int64_t tiles_m = grouped ? (g.M + kBM - 1) / kBM + g.G : (g.M + kBM - 1) / kBM;
   const int64_t nblocks = tiles_m * kp.tiles_n;

@@ -61,5 +61,7 @@ struct GemmArgs {
   int64_t b_gs, sb_gs;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// Rows of A per workgroup tile of the GEMM kernels.
+int64_t gemm_tile_m();
 
 }  // namespace fp8fg

@@ -5,6 +5,11 @@ Layouts (row-major, last index contiguous):
   quantize_1x128(x [M][K])            -> q u8 [M][K],  s f32 [M][K/128]
   quantize_128x1(x [T][F])            -> qT u8 [F][T], sT f32 [F][T/128]
   requantize_128x1(q [T][F], s [T][F/128]) -> same as quantize_128x1
+  Per-row tile scales are indexed s[row][group] in every case; by default
+  they are stored group-major (the returned tensor is a transposed view of
+  a [groups][rows] buffer, strides (1, rows)), so that the GEMM's per-group
+  load of consecutive rows' scales is one contiguous read.
+  scale_layout="row_major" stores them [rows][groups] instead.
   quantize_block(w [K][N], transpose) -> q u8 [N][K] (transpose) or [K][N],
                                          s f32 [K/128][N/128]
   gemm(qa [M][K], sa [M][K/128], qb [N][K], sb)  -> c [M][N]
@@ -24,33 +29,42 @@ def _rule(pow2):
     return B.FP8FG_SCALE_POW2 if pow2 else B.FP8FG_SCALE_AMAX
 
 
-def quantize_1x128(x, pow2=False, stream=None):
+def _scales(rows, groups, layout, device):
+    """Scale tensor indexed [row][group]."""
+    if layout == "group_major":
+        return torch.empty((groups, rows), dtype=torch.float32, device=device).t()
+    if layout == "row_major":
+        return torch.empty((rows, groups), dtype=torch.float32, device=device)
+    raise ValueError("scale_layout must be 'group_major' or 'row_major'")
+
+
+def quantize_1x128(x, pow2=False, scale_layout="group_major", stream=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    s = _scales(M, K // 128, scale_layout, x.device)
     B.fp8_quantize_rowtile(x, _XTYPE[x.dtype], M, K, x.stride(0), None, 0, 0,
-                           B.FP8FG_TILE_1x128, _rule(pow2), q, q.stride(0), s, s.stride(0), 1,
-                           stream)
+                           B.FP8FG_TILE_1x128, _rule(pow2), q, q.stride(0), s, s.stride(0),
+                           s.stride(1), stream)
     return q, s
 
 
-def quantize_128x1(x, pow2=False, stream=None):
+def quantize_128x1(x, pow2=False, scale_layout="group_major", stream=None):
     T, F = x.shape
     qt = torch.empty((F, T), dtype=torch.uint8, device=x.device)
-    st = torch.empty((F, T // 128), dtype=torch.float32, device=x.device)
+    st = _scales(F, T // 128, scale_layout, x.device)
     B.fp8_quantize_rowtile(x, _XTYPE[x.dtype], T, F, x.stride(0), None, 0, 0,
-                           B.FP8FG_TILE_128x1, _rule(pow2), qt, qt.stride(0), st, st.stride(0), 1,
-                           stream)
+                           B.FP8FG_TILE_128x1, _rule(pow2), qt, qt.stride(0), st, st.stride(0),
+                           st.stride(1), stream)
     return qt, st
 
 
-def requantize_128x1(q, s, pow2=False, stream=None):
+def requantize_128x1(q, s, pow2=False, scale_layout="group_major", stream=None):
     T, F = q.shape
     qt = torch.empty((F, T), dtype=torch.uint8, device=q.device)
-    st = torch.empty((F, T // 128), dtype=torch.float32, device=q.device)
+    st = _scales(F, T // 128, scale_layout, q.device)
     B.fp8_quantize_rowtile(q, B.FP8FG_E4M3, T, F, q.stride(0), s, s.stride(0), s.stride(1),
-                           B.FP8FG_TILE_128x1, _rule(pow2), qt, qt.stride(0), st, st.stride(0), 1,
-                           stream)
+                           B.FP8FG_TILE_128x1, _rule(pow2), qt, qt.stride(0), st, st.stride(0),
+                           st.stride(1), stream)
     return qt, st
 
 

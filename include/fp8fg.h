@@ -156,7 +156,12 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *       FP8_MFMA: P_kb comes from the FP8 MFMA (limited internal precision,
  *       see above); promotion and scaling as in the default path.
  *   Alignment: a, b 16-byte aligned, lda and ldb multiples of 16; c aligned
- *   to its element; scales 4-byte aligned.
+ *   to its element; scales 4-byte aligned.  (c 16-byte aligned with ldc a
+ *   multiple of 4 lets the kernel store 4 outputs per instruction.)
+ *   Limits (FP8FG_EUNSUPPORTED beyond them; the kernels address a tile with
+ *   32-bit offsets): lda < 2^23, ldb < 2^24, K < 2^31; when promoting,
+ *   sa_ms < 2^21 (and sb_ns < 2^21 in the COL mode) and
+ *   sa_ks * K/128, sb_ks * K/128 < 2^29.
  */
 FP8FG_API int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                          int64_t lda, const float* sa, int64_t sa_ms,

@@ -33,11 +33,11 @@ def rand_bits(rows, cols, seed, std=1.0, outliers=0.0, mult=1.0, uniform=False):
     return workloads.f32_to_bf16_bits(x)
 
 
-def dense_case(a_bits, b_bits, a_pow2=False, b_pow2=False, what=""):
+def dense_case(a_bits, b_bits, a_pow2=False, b_pow2=False, what="", scale_layout="group_major"):
     """Quantize on the GPU, check bytes, run both output types, compare."""
     ra = oracle.SCALE_POW2 if a_pow2 else oracle.SCALE_AMAX
     rb = oracle.SCALE_POW2 if b_pow2 else oracle.SCALE_AMAX
-    qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=a_pow2)
+    qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=a_pow2, scale_layout=scale_layout)
     qb, sb = T.quantize_block(bf16_dev(b_bits), pow2=b_pow2, transpose=True)
     qao, sao = oracle.quantize_1x128(f32(a_bits), ra)
     qbo, sbo = oracle.quantize_128x128(f32(b_bits), rb)
@@ -52,9 +52,10 @@ def dense_case(a_bits, b_bits, a_pow2=False, b_pow2=False, what=""):
     return h32, ref
 
 
-def test_workload1_full():
+@pytest.mark.parametrize("scale_layout", ["group_major", "row_major"])
+def test_workload1_full(scale_layout):
     w = workload(1)
-    dense_case(w["A"], w["B"], what="workload 1")
+    dense_case(w["A"], w["B"], what="workload 1", scale_layout=scale_layout)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 640), (129, 256, 256),

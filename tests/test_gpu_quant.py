@@ -88,9 +88,10 @@ def test_1x128_every_bf16_pattern(pow2, rule):
 
 @pytest.mark.parametrize("rows,cols", [(1, 128), (3, 384), (257, 1024), (128, 7168)])
 @pytest.mark.parametrize("pow2,rule", RULES)
-def test_1x128_shapes(rows, cols, pow2, rule):
+@pytest.mark.parametrize("scale_layout", ["group_major", "row_major"])
+def test_1x128_shapes(rows, cols, pow2, rule, scale_layout):
     bits = rand_bf16(rows, cols, seed=rows * 7 + cols)
-    q, s = T.quantize_1x128(bf16_dev(bits), pow2=pow2)
+    q, s = T.quantize_1x128(bf16_dev(bits), pow2=pow2, scale_layout=scale_layout)
     qo, so = oracle.quantize_1x128(f32(bits), rule)
     assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
 
@@ -151,10 +152,12 @@ def test_128x1_direct(rows, cols, pow2, rule):
 
 @pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (256, 640)])
 @pytest.mark.parametrize("pow2,rule", RULES)
-def test_128x1_requant(rows, cols, pow2, rule):
+@pytest.mark.parametrize("in_layout,out_layout", [("group_major", "group_major"), ("row_major", "row_major"),
+                                                  ("row_major", "group_major")])
+def test_128x1_requant(rows, cols, pow2, rule, in_layout, out_layout):
     bits = rand_bf16(rows, cols, seed=3 * rows + cols)
-    q1, s1 = T.quantize_1x128(bf16_dev(bits))
-    qt, st = T.requantize_128x1(q1, s1, pow2=pow2)
+    q1, s1 = T.quantize_1x128(bf16_dev(bits), scale_layout=in_layout)
+    qt, st = T.requantize_128x1(q1, s1, pow2=pow2, scale_layout=out_layout)
     q1o, s1o = oracle.quantize_1x128(f32(bits))
     assert np.array_equal(host(q1), q1o) and np.array_equal(host(s1), s1o)
     qo, so = oracle.requantize_128x1(q1o, s1o, rule)
