@@ -33,6 +33,9 @@ DEVICE = [
     "--offload-arch=gfx950",
     # no packed-FP32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in architectural VGPRs: the GEMMs scale and promote
+    # them with VALU instructions every K group, which cannot read AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

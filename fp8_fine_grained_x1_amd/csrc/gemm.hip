@@ -178,6 +178,12 @@ __device__ __forceinline__ void grouped_order(int id, int tiles_m, int tiles_n, 
   tn = in / gm;
 }
 
+// True when the FP32 product s = a * b of two nonzero scales lies below the
+// normal range (it then carries fewer than 24 significant bits).
+__device__ __forceinline__ bool scale_product_inexact(float a, float b, float s) {
+  return __builtin_fabsf(s) < 1.17549435e-38f && a != 0.f && b != 0.f;
+}
+
 // Round to nearest even (hardware conversion; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
@@ -478,15 +484,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // promotion: tile i's row scale is one value per lane
+      // promotion: tile i's row scale is one value per lane.  A scale
+      // product below the FP32 normal range would lose precision, so a wave
+      // with such a lane applies the two factors one after the other.
       if constexpr (BMODE == 0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const float s = sr.sa[i] * sr.sb;
+          if (__builtin_amdgcn_ballot_w64(scale_product_inexact(sr.sa[i], sr.sb, s)) == 0) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[i][j][r], s, acc[i][j][r]);
+              for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[i][j][r], s, acc[i][j][r]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[i][j][r] * sr.sa[i], sr.sb, acc[i][j][r]);
+          }
         }
       } else {
 #pragma unroll
@@ -499,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
             for (int i = 0; i < 2; ++i)
 #pragma unroll
               for (int t = 0; t < 4; ++t)
-                acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t], sr.sa[i] * cv[t], acc[i][j][4 * q + t]);
+                acc[i][j][4 * q + t] = __builtin_fmaf(P[i][j][4 * q + t] * sr.sa[i], cv[t], acc[i][j][4 * q + t]);
           }
       }
     };
@@ -587,6 +602,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
 #pragma unroll
             for (int r = 0; r < 4; ++r) cv[j][r] = sr.sb;
         }
+        // block scales: one product per row tile unless some lane's product
+        // lies below the FP32 normal range; column scales: the two factors
+        // one after the other
+        bool split = BMODE == 1;
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BMODE == 0) {
+          bool bad = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[i] = sr.sa[i] * sr.sb;
+            bad = bad || scale_product_inexact(sr.sa[i], sr.sb, s[i]);
+          }
+          split = __builtin_amdgcn_ballot_w64(bad) != 0;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -594,9 +623,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
             if ((j * 4 + i) % 2 == 0 && (j * 4 + i) / 2 < kDmaPerGroup) issue_one(kb + 2, Nx, (j * 4 + i) / 2);
             const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 bf[j], af[i], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+            if (split) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[i][j][r] = __builtin_fmaf(P[r], sr.sa[i] * cv[j][r], acc[i][j][r]);
+              for (int r = 0; r < 4; ++r)
+                acc[i][j][r] = __builtin_fmaf(P[r] * sr.sa[i], cv[j][r], acc[i][j][r]);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[r], s[i], acc[i][j][r]);
+            }
           }
         }
       }
@@ -630,6 +664,315 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
       }
     }
   }
+}
+
+// ===========================================================================
+// Default path for 128x128 B block scales and N % 256 == 0: rescaled
+// accumulation on 256x256 tiles.
+//
+// The group scale of output row m under the 128-column block of wave wn is
+// sigma_kb = sa(m, kb) * sb(kb, n / 128), one value per lane and row tile.  The
+// FP32 accumulator D holds the running sum in units of the current group's
+// scale: before the group's products are added (by the MFMA itself),
+//   D <- D * (sigma_{kb-1} / sigma_kb),
+// and the epilogue writes C = sigma_last * D.  This applies every group's
+// scales to full FP32 accumulators once per 128 of K, as the separate-P
+// form does, with one multiply per element and group, but without a second
+// set of accumulators -- which is what makes a 64x128 wave tile fit.
+// A group whose scale is below 2^-64 of the largest scale already seen in
+// the row is dropped (its products enter with the converter's 2^-127 factor
+// instead of 1); its true contribution is below 2^-39 of that row's largest
+// group term, and dropping it keeps D from overflowing.  The two scale
+// factors are kept apart (their product can be an FP32 denormal, which
+// would cost precision) and combined through mantissas and exponents.
+constexpr int kRBN = 256;
+constexpr int kRDmaA = kBM / (8 * kWaves);
+constexpr int kRDmaB = kRBN / (8 * kWaves);
+constexpr int kDropExp = 64;  // a group 2^64 below the largest so far is dropped
+
+struct __align__(16) Stage2 {
+  uint8_t a[kBM * kBK];
+  uint8_t b[kRBN * kBK];
+};
+
+template <int CT, bool GROUPED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
+  // Two stages, each its own LDS object (the K loop is unrolled by two).
+  __shared__ Stage2 stage0;
+  __shared__ Stage2 stage1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave >> 1;  // rows wm*64 .. +64
+  const int wn = wave & 1;   // columns wn*128 .. +128 (one B scale block)
+
+  // ---- tile decode
+  const int id = xcd_remap(blockIdx.x, p.nblocks);
+  const uint8_t* A = p.a;
+  const uint8_t* B = p.b;
+  const float* SB = p.sb;
+  int64_t row_base = 0;
+  int rows_valid = 0;
+  int tn = 0;
+  if constexpr (GROUPED) {
+    int t = id;
+    int e = 0;
+    bool found = false;
+    for (; e < p.G; ++e) {
+      const int64_t seg0 = p.offsets[e];
+      const int64_t seg1 = p.offsets[e + 1];
+      const int tm_e = (int)((seg1 - seg0 + kBM - 1) / kBM);
+      const int cnt = tm_e * p.tiles_n;
+      if (t < cnt) {
+        int tm;
+        grouped_order(t, tm_e, p.tiles_n, tm, tn);
+        row_base = seg0 + (int64_t)tm * kBM;
+        const int64_t rem = seg1 - row_base;
+        rows_valid = rem < kBM ? (int)rem : kBM;
+        found = true;
+        break;
+      }
+      t -= cnt;
+    }
+    if (!found) return;
+    B += (int64_t)e * p.b_gs;
+    SB += (int64_t)e * p.sb_gs;
+  } else {
+    const int tiles_m = (int)((p.M + kBM - 1) / kBM);
+    int tm;
+    grouped_order(id, tiles_m, p.tiles_n, tm, tn);
+    row_base = (int64_t)tm * kBM;
+    const int64_t rem = p.M - row_base;
+    rows_valid = rem < kBM ? (int)rem : kBM;
+  }
+  const int64_t n0 = (int64_t)tn * kRBN;
+  const int nkb = (int)(p.K / kBK);
+
+  // ---- copy sources: instruction i of wave w fills LDS rows (8i + w) * 8 .. +8
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kRBN * p.ldb));
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(p.a, 0u);
+  uint32_t a_off[kRDmaA], b_off[kRDmaB];
+#pragma unroll
+  for (int i = 0; i < kRDmaA; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    const int ra = r < rows_valid ? r : rows_valid - 1;  // ragged M: repeat the last row
+    a_off[i] = (uint32_t)(ra * p.lda + (((lane & 7) ^ swz(r)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < kRDmaB; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    b_off[i] = (uint32_t)(r * p.ldb + (((lane & 7) ^ swz(r)) << 4));
+  }
+  // Every group issues the same copies (empty ones past the last group).
+  auto issue = [&](int kb, Stage2& S) {
+    const bool live = kb < nkb;
+    const uint32_t koff = live ? (uint32_t)kb * kBK : 0u;
+    const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : null_rsrc;
+    const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : null_rsrc;
+#pragma unroll
+    for (int i = 0; i < kRDmaA; ++i) dma16(ra, a_off[i], koff, S.a + (i * kWaves + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < kRDmaB; ++i) dma16(rb, b_off[i], koff, S.b + (i * kWaves + wave) * 1024);
+  };
+
+  // ---- scale sources: this lane's output row in row tile i is wm*64 + i*32 + lane % 32
+  const int g = lane >> 5;
+  const int lr = lane & 31;
+  const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(p.sa + row_base * p.sa_ms, 0xFFFFFFFFu);
+  uint32_t sa_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wm * 64 + i * 32 + lr;
+    sa_off[i] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * p.sa_ms * 4);
+  }
+  const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(SB + ((n0 >> 7) + wn) * p.sb_ns, 0xFFFFFFFFu);
+  struct ScaleRegs {
+    float sa[2];
+    float sb;
+  };
+  auto load_scales = [&](int kb, ScaleRegs& s) {
+    const bool live = kb < nkb;
+    const __amdgpu_buffer_rsrc_t ra = live ? sa_rsrc : null_rsrc;
+    const __amdgpu_buffer_rsrc_t rb = live ? sb_rsrc : null_rsrc;
+    const uint32_t ka = live ? (uint32_t)(kb * p.sa_ks * 4) : 0u;
+    const uint32_t kbo = live ? (uint32_t)(kb * p.sb_ks * 4) : 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s.sa[i] = load_f32(ra, sa_off[i], ka);
+    s.sb = load_f32(rb, 0u, kbo);
+  };
+
+  // Wave tile 64x128 = 2x4 tiles of 32x32.  B is the first MFMA operand, so
+  // accumulator element r of lane l is row lr of row tile i and column
+  // 8 (r / 4) + 4 g + r % 4 of column tile j.
+  v16f D[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) D[i][j][r] = 0.f;
+  // D of row tile i is expressed in units of mc[i] * 2^ec[i], the product of
+  // the current group's two scales split into a mantissa product in
+  // [0.25, 1) and an exponent (the FP32 product itself may be a denormal);
+  // mc = 0 before anything was accumulated.  emax[i] is the largest exponent
+  // of a scale product taken so far.
+  float mc[2] = {0.f, 0.f};
+  int ec[2] = {0, 0};
+  int emax[2] = {-(1 << 20), -(1 << 20)};
+
+  // Top of group kb: the copies issued in group kb - 1 (this group's data)
+  // are the newest memory operations, so wait for all;
+  // after the barrier every wave's copies have landed and every wave has
+  // finished reading the other stage.
+  auto wait_group = [&]() {
+    wait_vmcnt<0>();
+    block_barrier();
+  };
+
+  // Rescale factors rs and A conversion scales cs of a group (one per lane
+  // and row tile): rs = (mc / m) * 2^(ec - e) for the group's scale product
+  // m * 2^e; the mantissa quotient lies in (0.25, 4), so nothing overflows
+  // before the exponent is applied (the reciprocal is refined by one Newton
+  // step).  They are computed at the end of the previous group, off the
+  // critical path.
+  float rs[2], cs[2];
+  auto factors = [&](const ScaleRegs& sr) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float a = sr.sa[i], b = sr.sb;
+      const float m = __builtin_amdgcn_frexp_mantf(a) * __builtin_amdgcn_frexp_mantf(b);
+      const int e = __builtin_amdgcn_frexp_expf(a) + __builtin_amdgcn_frexp_expf(b);
+      const bool drop = a == 0.f || b == 0.f || e < emax[i] - kDropExp;
+      float r = __builtin_amdgcn_rcpf(m);
+      r = __builtin_fmaf(__builtin_fmaf(-m, r, 1.0f), r, r);
+      rs[i] = drop ? 1.0f : __builtin_amdgcn_ldexpf(mc[i] * r, ec[i] - e);
+      cs[i] = drop ? 0.0f : 1.0f;
+      mc[i] = drop ? mc[i] : m;
+      ec[i] = drop ? ec[i] : e;
+      emax[i] = drop ? emax[i] : (e > emax[i] ? e : emax[i]);
+    }
+  };
+
+  // Group kb loads the scales of group kb + 2 into the register set that
+  // held group kb's (consumed at the end of group kb - 1), and at its end
+  // forms the factors of group kb + 1 from scales loaded a group earlier.
+  auto group = [&](int kb, const Stage2& S, Stage2& Nx, ScaleRegs& lsr, const ScaleRegs& fsr) {
+    wait_group();
+    uint4 ra[4][2], rb[4][4];
+    auto read_chunk = [&](int c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + lr;
+        ra[c][i] = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wn * 128 + j * 32 + lr;
+        rb[c][j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
+      }
+    };
+    v8bf af[2][2], bfr[2][4];  // [step parity][tile]
+    auto cvt8 = [](uint32_t lo, uint32_t hi, float sc) {
+      union {
+        v2bf p[4];
+        v8bf v;
+      } u;
+      u.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, false);
+      u.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, true);
+      u.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, false);
+      u.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, true);
+      return u.v;
+    };
+    auto convert = [&](int st) {
+      const int c = st >> 1, h = st & 1, par = st & 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[par][i] = h ? cvt8(ra[c][i].z, ra[c][i].w, cs[i]) : cvt8(ra[c][i].x, ra[c][i].y, cs[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[par][j] = h ? cvt8(rb[c][j].z, rb[c][j].w, 1.0f) : cvt8(rb[c][j].x, rb[c][j].y, 1.0f);
+    };
+    read_chunk(0);
+    read_chunk(1);
+    __builtin_amdgcn_sched_barrier(0);
+    // scales of group kb + 2 and copies of group kb + 1 (into the other stage)
+    load_scales(kb + 2, lsr);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 1, Nx);
+    __builtin_amdgcn_sched_barrier(0);
+    // the rescale runs while the fragment reads are in flight
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) D[i][j][r] *= rs[i];
+    convert(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int par = st & 1;
+      // chunk c + 1 is read at step 2c, one step before its first conversion
+      if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) read_chunk((st >> 1) + 1);
+      if (st + 1 < 8) convert(st + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          D[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[par][j], af[par][i], D[i][j], 0, 0, 0);
+        }
+      if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (st + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next group's factors, while this group's last MFMAs run
+    factors(fsr);
+  };
+
+  ScaleRegs sr0{}, sr1{};
+  load_scales(0, sr0);
+  load_scales(1, sr1);
+  issue(0, stage0);
+  factors(sr0);
+  int kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    group(kb, stage0, stage1, sr0, sr1);
+    group(kb + 1, stage1, stage0, sr1, sr0);
+  }
+  if (kb < nkb) group(kb, stage0, stage1, sr0, sr1);
+  wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
+
+  // ---- epilogue: C = D * mc * 2^ec; lane holds row lr of row tile i,
+  // columns 8q + 4g .. +3 of column tile j
+  const bool vec = p.vec_store != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = wm * 64 + i * 32 + lr;
+    if (row >= rows_valid) continue;
+    const int64_t grow = row_base + row;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i], ec[i]);
+        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+      }
+  }
+}
+
+template <int CT, bool GROUPED>
+hipError_t launch_rescale(const KParams& kp, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_rescale_kernel<CT, GROUPED>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
+  return hipGetLastError();
 }
 
 template <int CT, int BMODE, int MODE, bool GROUPED>
@@ -678,7 +1021,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   kp.b_gs = g.b_gs;
   kp.sb_gs = g.sb_gs;
   kp.G = (int)g.G;
-  kp.tiles_n = (int)(g.N / kBN);
+  const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION) ? kModeFp8NoPromo
+                   : (g.flags & FP8FG_GEMM_FP8_MFMA)   ? kModeFp8
+                                                        : kModeExact;
+  // the rescaled-accumulation kernel covers the default path with block
+  // scales on 256-column tiles
+  const bool rescale = mode == kModeExact && g.b_scale_mode == 0 && g.N % kRBN == 0;
+  kp.tiles_n = (int)(g.N / (rescale ? kRBN : kBN));
   const int esize = g.c_type == 0 ? 2 : 4;
   kp.vec_store = (reinterpret_cast<uintptr_t>(g.c) % (4 * esize) == 0) && (g.ldc % 4 == 0);
   const bool grouped = g.G > 0;
@@ -686,9 +1035,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int64_t nblocks = tiles_m * kp.tiles_n;
   if (nblocks == 0) return hipSuccess;
   kp.nblocks = (int)nblocks;
-  const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION) ? kModeFp8NoPromo
-                   : (g.flags & FP8FG_GEMM_FP8_MFMA)   ? kModeFp8
-                                                        : kModeExact;
+  if (rescale) {
+    if (g.c_type == 0) return grouped ? launch_rescale<0, true>(kp, st) : launch_rescale<0, false>(kp, st);
+    return grouped ? launch_rescale<1, true>(kp, st) : launch_rescale<1, false>(kp, st);
+  }
   if (g.c_type == 0) {
     return g.b_scale_mode == 0 ? launch_mode<0, 0>(kp, mode, grouped, st)
                                : launch_mode<0, 1>(kp, mode, grouped, st);

@@ -88,6 +88,68 @@ def test_identity_weights_bit_exact():
     assert np.array_equal(c32, expect)
 
 
+def _extreme_rows(M, K, seed):
+    """A [M][K] whose rows mix zero groups, groups 1e-25 / 1e-30 below their
+    neighbours, rising and falling scales, and rows tiny throughout."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    g = K // 128
+    f = np.ones((M, g), dtype=np.float32)
+    f[0:32, 0] = 0.0
+    f[32:64, 3] = 0.0
+    f[64:96, 2] = 1e-25
+    f[96:128, 5] = 1e-30
+    f[128:160, :] = np.logspace(-30, 0, g)
+    f[160:192, :] = np.logspace(0, -20, g)
+    f[192:224, :] = 1e-36
+    f[224:256, ::2] = 0.0
+    return x * np.repeat(f, 128, axis=1)
+
+
+def _check_rows(c, ref):
+    c = np.asarray(c, np.float64)
+    assert np.all(np.isfinite(c))
+    for r in range(ref.shape[0]):
+        nr = np.linalg.norm(ref[r])
+        if nr == 0:
+            assert np.all(c[r] == 0), r
+            continue
+        err = np.linalg.norm(c[r] - ref[r]) / nr
+        assert err <= 1e-5, (r, err)
+
+
+@pytest.mark.parametrize("N", [512, 384])
+def test_extreme_group_scales_per_row(N):
+    """Every row must match the oracle to 1e-5 relative to its own norm,
+    however its group scales vary (N = 512 runs the 256-column kernel,
+    N = 384 the 128-column one)."""
+    M, K = 256, 1024
+    x = _extreme_rows(M, K, 31)
+    w = (np.random.default_rng(32).standard_normal((K, N)) * 0.02).astype(np.float32)
+    qa, sa = T.quantize_1x128(f32_dev(x))
+    qb, sb = T.quantize_block(f32_dev(w))
+    qao, sao = oracle.quantize_1x128(x)
+    qbo, sbo = oracle.quantize_128x128(w)
+    assert np.array_equal(host(qa), qao) and np.array_equal(host(sa), sao)
+    c = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+    _check_rows(c, oracle.gemm_blockscaled(qao, sao, qbo, sbo))
+
+
+def test_extreme_group_scales_per_row_column_scales():
+    """The same rows through the per-column-scale (wgrad) layout."""
+    M, K, N = 256, 1024, 256
+    a = _extreme_rows(M, K, 33)
+    x = np.ascontiguousarray(a.T)                     # X [T=K][F=M]
+    dy = np.random.default_rng(34).standard_normal((K, N)).astype(np.float32)
+    qx, sx = T.quantize_128x1(f32_dev(x))
+    qd, sd = T.quantize_128x1(f32_dev(dy))
+    qxo, sxo = oracle.quantize_128x1(x)
+    qdo, sdo = oracle.quantize_128x1(dy)
+    assert np.array_equal(host(qx), qxo.T) and np.array_equal(host(sx), sxo.T)
+    c = host(T.gemm(qx, sx, qd, sd, out_dtype=torch.float32, col_scales=True))
+    _check_rows(c, oracle.wgrad(qxo, sxo, qdo, sdo))
+
+
 def test_strided_output_and_guard_bands():
     M, N, K = 130, 256, 384
     a = rand_bits(M, K, seed=8)
