@@ -111,7 +111,8 @@ struct KParams {
   int G;
   int tiles_n;
   int nblocks;
-  int vec_store;  // c rows allow 4-element vector stores
+  int vec_store;   // c rows allow 4-element vector stores
+  int64_t n_base;  // first output column of this launch's tiles
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -667,45 +668,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
 }
 
 // ===========================================================================
-// Default path for 128x128 B block scales and N % 256 == 0: rescaled
-// accumulation on 256x256 tiles.
+// Default path (exact partial sums, 128x128 B block scales): rescaled
+// accumulation on 256 x (64 JT) tiles, JT = 4 (256 columns) or 3 (192).
 //
-// The group scale of output row m under the 128-column block of wave wn is
-// sigma_kb = sa(m, kb) * sb(kb, n / 128), one value per lane and row tile.  The
-// FP32 accumulator D holds the running sum in units of the current group's
-// scale: before the group's products are added (by the MFMA itself),
+// The group scale of output element (m, n) is sigma_kb = sa(m, kb) *
+// sb(kb, n / 128).  The FP32 accumulator D holds the running sum in units of
+// the current group's scale: before the group's products are added (by the
+// MFMA itself),
 //   D <- D * (sigma_{kb-1} / sigma_kb),
 // and the epilogue writes C = sigma_last * D.  This applies every group's
 // scales to full FP32 accumulators once per 128 of K, as the separate-P
 // form does, with one multiply per element and group, but without a second
-// set of accumulators -- which is what makes a 64x128 wave tile fit.
-// A group whose scale is below 2^-64 of the largest scale already seen in
-// the row is dropped (its products enter with the converter's 2^-127 factor
-// instead of 1); its true contribution is below 2^-39 of that row's largest
-// group term, and dropping it keeps D from overflowing.  The two scale
-// factors are kept apart (their product can be an FP32 denormal, which
-// would cost precision) and combined through mantissas and exponents.
-constexpr int kRBN = 256;
-constexpr int kRDmaA = kBM / (8 * kWaves);
-constexpr int kRDmaB = kRBN / (8 * kWaves);
-constexpr int kDropExp = 64;  // a group 2^64 below the largest so far is dropped
+// set of accumulators -- which is what makes a 64x(32 JT) wave tile fit.
+// The scale is kept as a mantissa product in [0.25, 1) and an exponent
+// (the FP32 product of the two scales can be a denormal, which would cost
+// precision), and the per-group ratio is formed from them so that nothing
+// overflows on the way.  D's units never go below 2^-64 of the largest
+// scale taken so far: a group with a smaller scale is accumulated in those
+// floor units instead of its own.  Its products then enter with a weight at
+// most 2^-64 of that largest scale where the true weight is smaller still,
+// so the difference is below 2^-39 of the largest group term; and D stays
+// bounded (each group adds less than 2^91 units, so |D| < 2^115 for K < 2^31).
+//
+// JT = 4: the 128 columns of a wave lie in one B scale block (tiles start at
+// multiples of 256), so sigma is one value per lane and row tile.  JT = 3: a
+// wave's 96 columns can straddle two B blocks, so sigma is tracked per row
+// tile and column tile.
+constexpr int kDropExp = 64;  // floor of D's units: 2^-64 of the largest scale taken
 
+template <int JT>
 struct __align__(16) Stage2 {
   uint8_t a[kBM * kBK];
-  uint8_t b[kRBN * kBK];
+  uint8_t b[64 * JT * kBK];
 };
 
-template <int CT, bool GROUPED>
+template <int CT, bool GROUPED, int JT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
+  constexpr int kBNT = 64 * JT;         // workgroup tile columns
+  constexpr int kWN = 32 * JT;          // wave tile columns
+  constexpr bool kPerJ = JT != 4;
+  constexpr int kDmaA = kBM / (8 * kWaves);
+  constexpr int kDmaB = kBNT / (8 * kWaves);
   // Two stages, each its own LDS object (the K loop is unrolled by two).
-  __shared__ Stage2 stage0;
-  __shared__ Stage2 stage1;
+  __shared__ Stage2<JT> stage0;
+  __shared__ Stage2<JT> stage1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave >> 1;  // rows wm*64 .. +64
-  const int wn = wave & 1;   // columns wn*128 .. +128 (one B scale block)
+  const int wn = wave & 1;   // columns wn*kWN .. +kWN
 
   // ---- tile decode
   const int id = xcd_remap(blockIdx.x, p.nblocks);
@@ -746,40 +758,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
     const int64_t rem = p.M - row_base;
     rows_valid = rem < kBM ? (int)rem : kBM;
   }
-  const int64_t n0 = (int64_t)tn * kRBN;
+  const int64_t n0 = p.n_base + (int64_t)tn * kBNT;
   const int nkb = (int)(p.K / kBK);
 
   // ---- copy sources: instruction i of wave w fills LDS rows (8i + w) * 8 .. +8
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
-  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kRBN * p.ldb));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kBNT * p.ldb));
   const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(p.a, 0u);
-  uint32_t a_off[kRDmaA], b_off[kRDmaB];
+  uint32_t a_off[kDmaA], b_off[kDmaB];
 #pragma unroll
-  for (int i = 0; i < kRDmaA; ++i) {
+  for (int i = 0; i < kDmaA; ++i) {
     const int r = (i * kWaves + wave) * 8 + (lane >> 3);
     const int ra = r < rows_valid ? r : rows_valid - 1;  // ragged M: repeat the last row
     a_off[i] = (uint32_t)(ra * p.lda + (((lane & 7) ^ swz(r)) << 4));
   }
 #pragma unroll
-  for (int i = 0; i < kRDmaB; ++i) {
+  for (int i = 0; i < kDmaB; ++i) {
     const int r = (i * kWaves + wave) * 8 + (lane >> 3);
     b_off[i] = (uint32_t)(r * p.ldb + (((lane & 7) ^ swz(r)) << 4));
   }
   // Every group issues the same copies (empty ones past the last group).
-  auto issue = [&](int kb, Stage2& S) {
+  auto issue = [&](int kb, Stage2<JT>& S) {
     const bool live = kb < nkb;
     const uint32_t koff = live ? (uint32_t)kb * kBK : 0u;
     const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : null_rsrc;
     const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : null_rsrc;
 #pragma unroll
-    for (int i = 0; i < kRDmaA; ++i) dma16(ra, a_off[i], koff, S.a + (i * kWaves + wave) * 1024);
+    for (int i = 0; i < kDmaA; ++i) dma16(ra, a_off[i], koff, S.a + (i * kWaves + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < kRDmaB; ++i) dma16(rb, b_off[i], koff, S.b + (i * kWaves + wave) * 1024);
+    for (int i = 0; i < kDmaB; ++i) dma16(rb, b_off[i], koff, S.b + (i * kWaves + wave) * 1024);
   };
 
-  // ---- scale sources: this lane's output row in row tile i is wm*64 + i*32 + lane % 32
+  // ---- scale sources: this lane's output row in row tile i is wm*64 + i*32 + lane % 32;
+  // column tile j of the wave lies in B scale block (n0 + wn*kWN + 32 j) / 128
   const int g = lane >> 5;
   const int lr = lane & 31;
+  constexpr int NB = kPerJ ? JT : 1;  // B scales per group and wave
   const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(p.sa + row_base * p.sa_ms, 0xFFFFFFFFu);
   uint32_t sa_off[2];
 #pragma unroll
@@ -787,80 +801,109 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
     const int r = wm * 64 + i * 32 + lr;
     sa_off[i] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * p.sa_ms * 4);
   }
-  const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(SB + ((n0 >> 7) + wn) * p.sb_ns, 0xFFFFFFFFu);
+  __amdgpu_buffer_rsrc_t sb_rsrc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    sb_rsrc[j] = make_rsrc(SB + ((n0 + wn * kWN + 32 * j) >> 7) * p.sb_ns, 0xFFFFFFFFu);
   struct ScaleRegs {
     float sa[2];
-    float sb;
+    float sb[NB];
   };
   auto load_scales = [&](int kb, ScaleRegs& s) {
     const bool live = kb < nkb;
     const __amdgpu_buffer_rsrc_t ra = live ? sa_rsrc : null_rsrc;
-    const __amdgpu_buffer_rsrc_t rb = live ? sb_rsrc : null_rsrc;
     const uint32_t ka = live ? (uint32_t)(kb * p.sa_ks * 4) : 0u;
     const uint32_t kbo = live ? (uint32_t)(kb * p.sb_ks * 4) : 0u;
 #pragma unroll
     for (int i = 0; i < 2; ++i) s.sa[i] = load_f32(ra, sa_off[i], ka);
-    s.sb = load_f32(rb, 0u, kbo);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s.sb[j] = load_f32(live ? sb_rsrc[j] : null_rsrc, 0u, kbo);
   };
 
-  // Wave tile 64x128 = 2x4 tiles of 32x32.  B is the first MFMA operand, so
-  // accumulator element r of lane l is row lr of row tile i and column
+  // Wave tile 64 x kWN = 2 x JT tiles of 32x32.  B is the first MFMA operand,
+  // so accumulator element r of lane l is row lr of row tile i and column
   // 8 (r / 4) + 4 g + r % 4 of column tile j.
-  v16f D[2][4];
+  v16f D[2][JT];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) D[i][j][r] = 0.f;
-  // D of row tile i is expressed in units of mc[i] * 2^ec[i], the product of
-  // the current group's two scales split into a mantissa product in
-  // [0.25, 1) and an exponent (the FP32 product itself may be a denormal);
-  // mc = 0 before anything was accumulated.  emax[i] is the largest exponent
-  // of a scale product taken so far.
-  float mc[2] = {0.f, 0.f};
-  int ec[2] = {0, 0};
-  int emax[2] = {-(1 << 20), -(1 << 20)};
+  // D of (row tile i, scale column c) is expressed in units of
+  // mc * 2^ec, split into a mantissa in [0.25, 1] and an exponent; mc = 0
+  // before anything was accumulated.  emax is the largest exponent of a
+  // scale product taken so far.  c = j when scales differ per column tile,
+  // else 0.
+  float mc[2][NB], rs[2][NB];
+  int ec[2][NB], emax[2][NB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      mc[i][j] = 0.f;
+      rs[i][j] = 1.f;
+      ec[i][j] = 0;
+      emax[i][j] = -(1 << 20);
+    }
 
   // Top of group kb: the copies issued in group kb - 1 (this group's data)
-  // are the newest memory operations, so wait for all;
-  // after the barrier every wave's copies have landed and every wave has
-  // finished reading the other stage.
+  // are the newest memory operations, so wait for all; after the barrier
+  // every wave's copies have landed and every wave has finished reading the
+  // other stage.
   auto wait_group = [&]() {
     wait_vmcnt<0>();
     block_barrier();
   };
 
-  // Rescale factors rs and A conversion scales cs of a group (one per lane
-  // and row tile): rs = (mc / m) * 2^(ec - e) for the group's scale product
-  // m * 2^e; the mantissa quotient lies in (0.25, 4), so nothing overflows
-  // before the exponent is applied (the reciprocal is refined by one Newton
-  // step).  They are computed at the end of the previous group, off the
-  // critical path.
-  float rs[2], cs[2];
+  // Rescale factors of a group: rs = (mc / m) * 2^(ec - e) for the group's
+  // scale product m * 2^e; the mantissa quotient lies in (0.25, 4), so
+  // nothing overflows before the exponent is applied (the reciprocal is
+  // refined by one Newton step).  Computed at the end of the previous group,
+  // off the critical path.
   auto factors = [&](const ScaleRegs& sr) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float a = sr.sa[i], b = sr.sb;
-      const float m = __builtin_amdgcn_frexp_mantf(a) * __builtin_amdgcn_frexp_mantf(b);
-      const int e = __builtin_amdgcn_frexp_expf(a) + __builtin_amdgcn_frexp_expf(b);
-      const bool drop = a == 0.f || b == 0.f || e < emax[i] - kDropExp;
-      float r = __builtin_amdgcn_rcpf(m);
-      r = __builtin_fmaf(__builtin_fmaf(-m, r, 1.0f), r, r);
-      rs[i] = drop ? 1.0f : __builtin_amdgcn_ldexpf(mc[i] * r, ec[i] - e);
-      cs[i] = drop ? 0.0f : 1.0f;
-      mc[i] = drop ? mc[i] : m;
-      ec[i] = drop ? ec[i] : e;
-      emax[i] = drop ? emax[i] : (e > emax[i] ? e : emax[i]);
+      const float a = sr.sa[i];
+      const float ma = __builtin_amdgcn_frexp_mantf(a);
+      const int ea = __builtin_amdgcn_frexp_expf(a);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const float b = sr.sb[j];
+        float m = ma * __builtin_amdgcn_frexp_mantf(b);
+        int e = ea + __builtin_amdgcn_frexp_expf(b);
+        // below the floor (or a zero scale): accumulate in the floor units
+        const bool low = a == 0.f || b == 0.f || e < emax[i][j] - kDropExp;
+        m = low ? 1.0f : m;
+        e = low ? emax[i][j] - kDropExp : e;
+        float r = __builtin_amdgcn_rcpf(m);
+        r = __builtin_fmaf(__builtin_fmaf(-m, r, 1.0f), r, r);
+        rs[i][j] = __builtin_amdgcn_ldexpf(mc[i][j] * r, ec[i][j] - e);
+        mc[i][j] = m;
+        ec[i][j] = e;
+        emax[i][j] = e > emax[i][j] ? e : emax[i][j];
+      }
     }
+  };
+
+  auto cvt8 = [](uint32_t lo, uint32_t hi, float sc) {
+    union {
+      v2bf p[4];
+      v8bf v;
+    } u;
+    u.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, false);
+    u.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, true);
+    u.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, false);
+    u.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, true);
+    return u.v;
   };
 
   // Group kb loads the scales of group kb + 2 into the register set that
   // held group kb's (consumed at the end of group kb - 1), and at its end
   // forms the factors of group kb + 1 from scales loaded a group earlier.
-  auto group = [&](int kb, const Stage2& S, Stage2& Nx, ScaleRegs& lsr, const ScaleRegs& fsr) {
+  auto group = [&](int kb, const Stage2<JT>& S, Stage2<JT>& Nx, ScaleRegs& lsr, const ScaleRegs& fsr) {
     wait_group();
-    uint4 ra[4][2], rb[4][4];
+    uint4 ra[4][2], rb[4][JT];
     auto read_chunk = [&](int c) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -868,30 +911,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
         ra[c][i] = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + j * 32 + lr;
+      for (int j = 0; j < JT; ++j) {
+        const int row = wn * kWN + j * 32 + lr;
         rb[c][j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
       }
     };
-    v8bf af[2][2], bfr[2][4];  // [step parity][tile]
-    auto cvt8 = [](uint32_t lo, uint32_t hi, float sc) {
-      union {
-        v2bf p[4];
-        v8bf v;
-      } u;
-      u.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, false);
-      u.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, true);
-      u.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, false);
-      u.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, true);
-      return u.v;
-    };
+    v8bf af[2][2], bfr[2][JT];  // [step parity][tile]
     auto convert = [&](int st) {
       const int c = st >> 1, h = st & 1, par = st & 1;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[par][i] = h ? cvt8(ra[c][i].z, ra[c][i].w, cs[i]) : cvt8(ra[c][i].x, ra[c][i].y, cs[i]);
+        af[par][i] = h ? cvt8(ra[c][i].z, ra[c][i].w, 1.0f) : cvt8(ra[c][i].x, ra[c][i].y, 1.0f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JT; ++j)
         bfr[par][j] = h ? cvt8(rb[c][j].z, rb[c][j].w, 1.0f) : cvt8(rb[c][j].x, rb[c][j].y, 1.0f);
     };
     read_chunk(0);
@@ -906,33 +938,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) D[i][j][r] *= rs[i];
+        for (int r = 0; r < 16; ++r) D[i][j][r] *= rs[i][kPerJ ? j : 0];
     convert(0);
     __builtin_amdgcn_sched_barrier(0);
+    // the 8 K steps
+    auto steps = [&]() {
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int par = st & 1;
-      // chunk c + 1 is read at step 2c, one step before its first conversion
-      if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) read_chunk((st >> 1) + 1);
-      if (st + 1 < 8) convert(st + 1);
+      for (int st = 0; st < 8; ++st) {
+        const int par = st & 1;
+        // chunk c + 1 is read at step 2c, one step before its first conversion
+        if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) read_chunk((st >> 1) + 1);
+        if (st + 1 < 8) convert(st + 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JT; ++j)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          D[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[par][j], af[par][i], D[i][j], 0, 0, 0);
+          for (int i = 0; i < 2; ++i)
+            D[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[par][j], af[par][i], D[i][j], 0, 0, 0);
+        if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2 + JT, 0);
+#pragma unroll
+        for (int m = 0; m < 2 * JT; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (st + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
-      if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (st + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the next group's factors, while this group's last MFMAs run
-    factors(fsr);
+    };
+    steps();
+    // the next group's factors, while this group's last MFMAs run (none
+    // after the last group: the epilogue needs this group's units)
+    if (kb + 1 < nkb) factors(fsr);
   };
 
   ScaleRegs sr0{}, sr1{};
@@ -957,21 +993,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
     if (row >= rows_valid) continue;
     const int64_t grow = row_base + row;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+        const int64_t col = n0 + wn * kWN + j * 32 + 8 * q + 4 * g;
+        const int c = kPerJ ? j : 0;
         float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i], ec[i]);
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i][c], ec[i][c]);
         store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
       }
   }
 }
 
-template <int CT, bool GROUPED>
+template <int CT, bool GROUPED, int JT>
 hipError_t launch_rescale(const KParams& kp, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_rescale_kernel<CT, GROUPED>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
+  hipLaunchKernelGGL((gemm_rescale_kernel<CT, GROUPED, JT>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
   return hipGetLastError();
 }
 
@@ -1000,6 +1037,33 @@ hipError_t launch_mode(const KParams& kp, int mode, bool grouped, hipStream_t st
 
 int64_t gemm_tile_m() { return kBM; }
 
+ColumnPlan plan_columns(int64_t tiles_m, int64_t N, int cus) {
+  // Column tiles of 256 and 192 with 256 n256 + 192 n192 = N; the split
+  // with the fewest CU rounds (a 192-column tile costs 3/4 of a 256-column
+  // one) wins, ties going to more 256-column tiles.  cus <= 0: 256-column
+  // tiles only.
+  ColumnPlan best{0, 0};
+  if (N % 64 != 0 || N == 0) return best;
+  if (cus <= 0) {
+    if (N % 256 == 0) best.n256 = N / 256;
+    return best;
+  }
+  int64_t best_cost = -1;  // in quarter rounds
+  for (int64_t n256 = N / 256; n256 >= 0; --n256) {
+    const int64_t rem = N - 256 * n256;
+    if (rem % 192 != 0) continue;
+    const int64_t n192 = rem / 192;
+    const int64_t r256 = (tiles_m * n256 + cus - 1) / cus;
+    const int64_t r192 = (tiles_m * n192 + cus - 1) / cus;
+    const int64_t cost = 4 * r256 + 3 * r192;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ColumnPlan{n256, n192};
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   KParams kp;
   kp.M = g.M;
@@ -1024,21 +1088,42 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION) ? kModeFp8NoPromo
                    : (g.flags & FP8FG_GEMM_FP8_MFMA)   ? kModeFp8
                                                         : kModeExact;
-  // the rescaled-accumulation kernel covers the default path with block
-  // scales on 256-column tiles
-  const bool rescale = mode == kModeExact && g.b_scale_mode == 0 && g.N % kRBN == 0;
-  kp.tiles_n = (int)(g.N / (rescale ? kRBN : kBN));
   const int esize = g.c_type == 0 ? 2 : 4;
   kp.vec_store = (reinterpret_cast<uintptr_t>(g.c) % (4 * esize) == 0) && (g.ldc % 4 == 0);
+  kp.n_base = 0;
   const bool grouped = g.G > 0;
   const int64_t tiles_m = grouped ? (g.M + kBM - 1) / kBM + g.G : (g.M + kBM - 1) / kBM;
+  if (tiles_m == 0) return hipSuccess;
+  // The default path with block scales runs the rescaled-accumulation
+  // kernel on 256-column tiles and possibly a second launch of 192-column
+  // tiles, the split that fills the CUs best (for a grouped GEMM tiles_m
+  // counts the row tiles of the worst case).  Both tile widths compute
+  // every output element with the same operations in the same order.
+  if (mode == kModeExact && g.b_scale_mode == 0) {
+    const ColumnPlan plan = plan_columns(tiles_m, g.N, device_cu_count());
+    if (plan.n256 + plan.n192 > 0) {
+      hipError_t e = hipSuccess;
+      if (plan.n256 > 0) {
+        kp.tiles_n = (int)plan.n256;
+        kp.nblocks = (int)(tiles_m * plan.n256);
+        e = g.c_type == 0 ? (grouped ? launch_rescale<0, true, 4>(kp, st) : launch_rescale<0, false, 4>(kp, st))
+                          : (grouped ? launch_rescale<1, true, 4>(kp, st) : launch_rescale<1, false, 4>(kp, st));
+        if (e != hipSuccess) return e;
+      }
+      if (plan.n192 > 0) {
+        kp.n_base = 256 * plan.n256;
+        kp.tiles_n = (int)plan.n192;
+        kp.nblocks = (int)(tiles_m * plan.n192);
+        e = g.c_type == 0 ? (grouped ? launch_rescale<0, true, 3>(kp, st) : launch_rescale<0, false, 3>(kp, st))
+                          : (grouped ? launch_rescale<1, true, 3>(kp, st) : launch_rescale<1, false, 3>(kp, st));
+      }
+      return e;
+    }
+  }
+  kp.tiles_n = (int)(g.N / kBN);
   const int64_t nblocks = tiles_m * kp.tiles_n;
   if (nblocks == 0) return hipSuccess;
   kp.nblocks = (int)nblocks;
-  if (rescale) {
-    if (g.c_type == 0) return grouped ? launch_rescale<0, true>(kp, st) : launch_rescale<0, false>(kp, st);
-    return grouped ? launch_rescale<1, true>(kp, st) : launch_rescale<1, false>(kp, st);
-  }
   if (g.c_type == 0) {
     return g.b_scale_mode == 0 ? launch_mode<0, 0>(kp, mode, grouped, st)
                                : launch_mode<0, 1>(kp, mode, grouped, st);

@@ -63,5 +63,12 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 // Rows of A per workgroup tile of the GEMM kernels.
 int64_t gemm_tile_m();
+// Split of N into column tiles of 256 and 192 for the default GEMM path
+// (both zero: the path does not apply).  cus = 0 asks for 256-column tiles
+// only (grouped GEMM).
+struct ColumnPlan {
+  int64_t n256, n192;
+};
+ColumnPlan plan_columns(int64_t tiles_m, int64_t N, int cus);
 
 }  // namespace fp8fg

@@ -268,8 +268,12 @@ def sample_rows(M, seed, n=40):
 
 
 def sample_blocks(N, seed):
+    # first, last and a random 128-column block, plus blocks 31..33: with
+    # M = 4096 and N = 7168 the dense kernel switches from 256- to 192-column
+    # tiles at column 4096, and block 33 straddles two 192-column tiles
     rng = np.random.default_rng(seed + 1000)
-    return sorted({0, N // 128 - 1, int(rng.integers(N // 128))})
+    nb = N // 128
+    return sorted({0, nb - 1, int(rng.integers(nb))} | {b for b in (31, 32, 33) if b < nb})
 
 
 def dense_full_size(w, pow2_a=False):
