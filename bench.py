@@ -16,10 +16,12 @@ Printed: one JSON line.  `value` is whole-step throughput in GEMM TFLOP/s
 (2 M N K per step / wall time per step, quantizers included).  Per-kernel
 times come from HIP events recorded on the launch stream around every
 launch inside the timed region; `roofline` is the GEMM's (the dominant
-kernel): algorithmic 2 M N K flops per launch / its mean launch time,
-against the dense peak of the matrix instruction it runs (BF16: the FP8
-operands are converted exactly to BF16 in registers, because the FP8 matrix
-instruction truncates inside its 8-product groups).
+kernel): algorithmic 2 M N K flops per GEMM call / its mean time, against
+the dense peak of the matrix instruction it runs (BF16: the FP8 operands are
+converted exactly to BF16 in registers, because the FP8 matrix instruction
+truncates inside its 8-product groups).  On this shape one GEMM call is two
+back-to-back launches of the same kernel, on 256- and on 192-column tiles
+(4096 and 3072 of the 7168 columns); the events bracket both.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
     python bench.py --copy-calibration   # plain 1 GiB device copy, for the
@@ -62,8 +64,8 @@ def gemm_source_sha():
 
 
 def traffic_from_profile():
-    """HBM bytes per GEMM launch from the committed rocprofv3 PMC summary,
-    or None when absent or taken on a different kernel source."""
+    """HBM bytes per GEMM call (both launches) from the committed rocprofv3
+    PMC summary, or None when absent or taken on a different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -74,7 +76,7 @@ def traffic_from_profile():
     if kv.get("gemm_source_sha256") != gemm_source_sha():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_gemm_call"])
     except (KeyError, ValueError):
         return None
 

@@ -21,10 +21,10 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_needs_matching_kernel_source(tmp_path, monkeypatch):
     f = tmp_path / "traffic.txt"
-    f.write_text("# test\ngemm_source_sha256: %s\nhbm_bytes_per_launch: 123.0\n" % ("0" * 64))
+    f.write_text("# test\ngemm_source_sha256: %s\nhbm_bytes_per_gemm_call: 123.0\n" % ("0" * 64))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.traffic_from_profile() is None
-    f.write_text("gemm_source_sha256: %s\nhbm_bytes_per_launch: 123.0\n" % bench.gemm_source_sha())
+    f.write_text("gemm_source_sha256: %s\nhbm_bytes_per_gemm_call: 123.0\n" % bench.gemm_source_sha())
     assert bench.traffic_from_profile() == 123.0
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.txt"))
     assert bench.traffic_from_profile() is None
