@@ -233,6 +233,75 @@ def main():
 
     rq_ms = timed(requant)
     p2_ms = timed(pow2)
+
+    # Dgrad of a layer of the same shape, dX [M][K] = dY [M][N] . W^T: dY
+    # quantized 1x128 along N, W [K][N] block-quantized without the transpose
+    # (its rows, the output columns, are then contraction-contiguous).
+    d6 = workloads.workload_inputs(6)
+    dy6, w6 = to_dev(d6["dY"]), to_dev(d6["W"])
+    qdy6 = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sdy6 = torch.empty((N // 128, M), dtype=torch.float32, device=dev)       # group-major
+    qw6 = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    sw6 = torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev)
+    c6 = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    B.fp8_quantize_rowtile(dy6, B.FP8FG_BF16, M, N, N, None, 0, 0, B.FP8FG_TILE_1x128,
+                           B.FP8FG_SCALE_AMAX, qdy6, N, sdy6, 1, M, stream)
+    B.fp8_quantize_block(w6, B.FP8FG_BF16, K, N, N, B.FP8FG_SCALE_AMAX, 0, qw6, N,
+                         sw6, N // 128, 1, stream)
+    del dy6, w6
+
+    def dgrad():
+        B.fp8_gemm_blockscaled(M, K, N, qdy6, N, sdy6, 1, M, qw6, N, sw6, N // 128, 1,
+                               B.FP8FG_BSCALE_BLOCK128, c6, B.FP8FG_BF16, K, B.FP8FG_GEMM_DEFAULT,
+                               stream)
+
+    dg_ms = timed(dgrad)
+    del qdy6, sdy6, qw6, sw6, c6
+
+    def grouped_setup(w):
+        """FP8 operands of a grouped workload: 1x128 power-of-two activation
+        scales (group-major), per-expert 128x128 weight blocks, transposed."""
+        dw = workloads.workload_inputs(w)
+        spec = workloads.WORKLOADS[w]
+        Gx, Mx, Nx, Kx = spec["G"], spec["M"], spec["N"], spec["K"]
+        ax = to_dev(dw["A"])
+        o = dict(G=Gx, M=Mx, N=Nx, K=Kx,
+                 qa=torch.empty((Mx, Kx), dtype=torch.uint8, device=dev),
+                 sa=torch.empty((Kx // 128, Mx), dtype=torch.float32, device=dev),
+                 qb=torch.empty((Gx, Nx, Kx), dtype=torch.uint8, device=dev),
+                 sb=torch.empty((Gx, Kx // 128, Nx // 128), dtype=torch.float32, device=dev),
+                 c=torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev),
+                 off=torch.from_numpy(dw["offsets"].astype(np.int32)).to(dev),
+                 counts=dw["counts"].tolist())
+        B.fp8_quantize_rowtile(ax, B.FP8FG_BF16, Mx, Kx, Kx, None, 0, 0, B.FP8FG_TILE_1x128,
+                               B.FP8FG_SCALE_POW2, o["qa"], Kx, o["sa"], 1, Mx, stream)
+        for e in range(Gx):
+            we = to_dev(dw["W"][e])
+            B.fp8_quantize_block(we, B.FP8FG_BF16, Kx, Nx, Nx, B.FP8FG_SCALE_AMAX, 1, o["qb"][e], Kx,
+                                 o["sb"][e], Nx // 128, 1, stream)
+        torch.cuda.synchronize()
+        return o
+
+    def grouped(o):
+        B.fp8_grouped_gemm_blockscaled(o["G"], o["off"], o["M"], o["N"], o["K"], o["qa"], o["K"],
+                                       o["sa"], 1, o["M"], o["qb"], o["K"], o["N"] * o["K"], o["sb"],
+                                       1, o["N"] // 128, (o["K"] // 128) * (o["N"] // 128), o["c"],
+                                       B.FP8FG_BF16, o["N"], B.FP8FG_GEMM_DEFAULT, stream)
+
+    g7 = grouped_setup(7)
+    dn_ms = timed(lambda: grouped(g7))
+    dn_flops = 2.0 * g7["M"] * g7["N"] * g7["K"]
+    del g7
+    g8 = grouped_setup(8)
+    dc_ms = timed(lambda: grouped(g8))
+    dc_flops = 2.0 * g8["M"] * g8["N"] * g8["K"]
+    # algorithmic bytes of the decode call: every expert's weights and block
+    # scales once, the activations and their scales once, the bf16 output once
+    dc_bytes = (g8["G"] * g8["N"] * g8["K"] + g8["G"] * (g8["K"] // 128) * (g8["N"] // 128) * 4
+                + g8["M"] * g8["K"] + g8["M"] * (g8["K"] // 128) * 4 + g8["M"] * g8["N"] * 2)
+    dc_desc = "G=%d, %d tokens (%d-%d per expert), K=%d -> N=%d" % (
+        g8["G"], g8["M"], min(g8["counts"]), max(g8["counts"]), g8["K"], g8["N"])
+    del g8
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     gemm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
@@ -245,6 +314,9 @@ def main():
 
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
+
+    def tflops(nflops, ms):
+        return nflops / (ms * 1e-3) / 1e12
 
     out = {
         "metric": "block-scaled FP8 GEMM TFLOPS (% FP8 MFMA peak); quantize GB/s (% HBM)",
@@ -279,6 +351,17 @@ def main():
                 "ms": round(gemm_ms, 4), "TFLOP/s": round(gemm_tflops, 1),
                 "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                 "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
+            "fp8_gemm_blockscaled dgrad dX = dY.W^T, 4096x7168x7168 (outside the step)": {
+                "ms": round(dg_ms, 4), "TFLOP/s": round(tflops(flops, dg_ms), 1),
+                "frac_bf16_peak": round(tflops(flops, dg_ms) / PEAK_BF16_TFLOPS, 4)},
+            "fp8_grouped_gemm_blockscaled MoE down-projection G=8, 16384 tokens, K=4096 -> N=7168, "
+            "pow2 activation scales (outside the step)": {
+                "ms": round(dn_ms, 4), "TFLOP/s": round(tflops(dn_flops, dn_ms), 1),
+                "frac_bf16_peak": round(tflops(dn_flops, dn_ms) / PEAK_BF16_TFLOPS, 4)},
+            "fp8_grouped_gemm_blockscaled MoE decode %s (outside the step)" % dc_desc: {
+                "ms": round(dc_ms, 4), "GB/s": round(gbs(dc_bytes, dc_ms), 1),
+                "frac_hbm": round(gbs(dc_bytes, dc_ms) / PEAK_HBM_GBS, 3),
+                "TFLOP/s": round(tflops(dc_flops, dc_ms), 1)},
         },
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),

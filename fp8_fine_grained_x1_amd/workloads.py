@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five workloads.
+"""Seeded synthetic inputs for the workloads.
 
 This module only draws random numbers and stores them as bf16 bit patterns;
 it holds none of the method's arithmetic (no scales, no FP8, no GEMM).  Both
@@ -14,11 +14,12 @@ Recipe (identical for every consumer):
     replacement, multiplied by the factor), then each value is rounded to
     bf16 with round-to-nearest-even;
   * MoE token counts: multinomial(total, p_k proportional to k**-1.2,
-    k = 1..G), expert 0 taking rank 1.
+    k = 1..G), expert 0 taking rank 1 (Zipf workloads), or with equal p_k
+    (the decode workload).
 
 Arrays are returned as uint16 bf16 bit patterns, row-major, in the logical
 orientation of the problem: A [M][K], B [K][N], W [G][K][N], X [T][F],
-dY [T][N].
+dY [T][N] (workload 5) or [M][N] (workload 6).
 """
 
 import numpy as np
@@ -44,6 +45,20 @@ WORKLOADS = {
             T=8192, F=7168, N=4096,
             a=dict(dist="normal", std=1.0),      # X  [T][F]
             b=dict(dist="normal", std=1.0)),     # dY [T][N]
+    # dX [M][K] = dY [M][N] . W^T of the dense forward layer's shape
+    6: dict(name="backward input-gradient GEMM",
+            M=4096, N=7168, K=7168,
+            a=dict(dist="normal", std=1.0, outlier_frac=0.001, outlier_mult=100.0),  # dY [M][N]
+            b=dict(dist="normal", std=0.02)),                                         # W [K][N]
+    7: dict(name="MoE grouped down-projection",
+            M=16384, N=7168, K=4096, G=8, zipf=1.2,
+            a=dict(dist="normal", std=1.0),
+            b=dict(dist="normal", std=0.02)),
+    # few tokens per expert: the weights dominate the bytes moved
+    8: dict(name="MoE grouped up-projection, decode",
+            M=512, N=4096, K=7168, G=16, zipf=None,
+            a=dict(dist="normal", std=1.0),
+            b=dict(dist="normal", std=0.02)),
 }
 
 
@@ -91,8 +106,11 @@ def draw_bf16(shape, spec, seed, outlier_seed=None):
 def moe_token_counts(workload=4):
     w = WORKLOADS[workload]
     G, total, alpha = w["G"], w["M"], w["zipf"]
-    p = np.arange(1, G + 1, dtype=np.float64) ** (-alpha)
-    p /= p.sum()
+    if alpha is None:
+        p = np.full(G, 1.0 / G)
+    else:
+        p = np.arange(1, G + 1, dtype=np.float64) ** (-alpha)
+        p /= p.sum()
     rng = np.random.default_rng(seed_for(workload, 3))
     return rng.multinomial(total, p).astype(np.int64)
 
@@ -111,7 +129,7 @@ def workload_inputs(workload):
         out["A"] = draw_bf16((w["M"], w["K"]), w["a"], seed_for(workload, 0),
                              seed_for(workload, 2))
         out["B"] = draw_bf16((w["K"], w["N"]), w["b"], seed_for(workload, 1))
-    elif workload == 4:
+    elif workload in (4, 7, 8):
         out["A"] = draw_bf16((w["M"], w["K"]), w["a"], seed_for(workload, 0))
         out["W"] = draw_bf16((w["G"], w["K"], w["N"]), w["b"], seed_for(workload, 1))
         out["counts"] = moe_token_counts(workload)
@@ -119,6 +137,10 @@ def workload_inputs(workload):
     elif workload == 5:
         out["X"] = draw_bf16((w["T"], w["F"]), w["a"], seed_for(workload, 0))
         out["dY"] = draw_bf16((w["T"], w["N"]), w["b"], seed_for(workload, 1))
+    elif workload == 6:
+        out["dY"] = draw_bf16((w["M"], w["N"]), w["a"], seed_for(workload, 0),
+                              seed_for(workload, 2))
+        out["W"] = draw_bf16((w["K"], w["N"]), w["b"], seed_for(workload, 1))
     else:
         raise ValueError(workload)
     return out

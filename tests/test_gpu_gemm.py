@@ -335,12 +335,39 @@ def test_workload3_full_size_sampled_and_naive_gap():
             oracle.rel_frob(naive, truth), oracle.max_rel(naive, truth)))
 
 
-def test_workload4_grouped_full_size_sampled():
-    d = workload(4)
+def test_workload6_dgrad_full_size_sampled():
+    # dX = dY . W^T: dY quantized 1x128 along N (the contraction), W block-
+    # quantized without the transpose ([K][N] is K-major for this product:
+    # its rows are the output columns), its block scales read transposed
+    d = workload(6)
+    dy_bits, w_bits = d["dY"], d["W"]
+    M, N = dy_bits.shape
+    K = w_bits.shape[0]
+    say("workload 6: dX[%d][%d] = dY[%d][%d] . W^T, W[%d][%d]" % (M, K, M, N, K, N))
+    qd, sd = T.quantize_1x128(bf16_dev(dy_bits))
+    qw, sw = T.quantize_block(bf16_dev(w_bits), transpose=False)      # [K][N], [K/128][N/128]
+    c32 = T.gemm(qd, sd, qw, sw.t(), out_dtype=torch.float32)           # [M][K]
+    c16 = T.gemm(qd, sd, qw, sw.t(), out_dtype=torch.bfloat16)
+    rows = sample_rows(M, 6)
+    qdo, sdo = oracle.quantize_1x128(f32(dy_bits[rows]))
+    idx = torch.from_numpy(rows).to(DEV)
+    h32 = host(c32.index_select(0, idx))
+    h16 = host(c16.index_select(0, idx))
+    for blk in sample_blocks(K, 6):
+        cols = slice(blk * 128, (blk + 1) * 128)
+        # the oracle's B operand is W^T [N][K]; its 128x128 blocks are those of W
+        qbo, sbo = oracle.quantize_128x128(f32(w_bits[cols, :]).T)
+        ref = oracle.gemm_blockscaled(qdo, sdo, qbo, sbo)
+        check_gemm(h32[:, cols], ref, "workload 6 block %d" % blk)
+        check_bf16_output(h16[:, cols], h32[:, cols], ref)
+
+
+def grouped_full_size(w):
+    d = workload(w)
     a_bits, w_bits, counts, off = d["A"], d["W"], d["counts"], d["offsets"]
     G, K, N = w_bits.shape
     M = a_bits.shape[0]
-    say("workload 4: G=%d M=%d N=%d K=%d counts=%s" % (G, M, N, K, counts.tolist()))
+    say("workload %d: G=%d M=%d N=%d K=%d counts=%s" % (w, G, M, N, K, counts.tolist()))
     qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=True)
     qb = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
     sb = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device=DEV)
@@ -365,8 +392,20 @@ def test_workload4_grouped_full_size_sampled():
             cols = slice(blk * 128, (blk + 1) * 128)
             qbo, sbo = oracle.quantize_128x128(f32(w_bits[e][:, cols]))
             ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
-            check_gemm(h32[:, cols], ref, "workload 4 expert %d block %d" % (e, blk))
+            check_gemm(h32[:, cols], ref, "workload %d expert %d block %d" % (w, e, blk))
             check_bf16_output(h16[:, cols], h32[:, cols], ref)
+
+
+def test_workload4_grouped_full_size_sampled():
+    grouped_full_size(4)
+
+
+def test_workload7_grouped_down_projection_full_size_sampled():
+    grouped_full_size(7)
+
+
+def test_workload8_grouped_decode_full_size_sampled():
+    grouped_full_size(8)
 
 
 def test_workload5_wgrad_full_size_sampled():
