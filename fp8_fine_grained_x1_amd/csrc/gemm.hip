@@ -168,6 +168,27 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblocks) {
   return xcd * q + (xcd < r ? xcd : r) + local;
 }
 
+// Logical tile id of this workgroup, or -1 if it has none.  A grouped
+// launch is sized for the worst case (the sum of ceil(M_e / bm) is at most
+// ceil(M / bm) + G row tiles): the tiles that exist are counted from the
+// offsets, workgroups past that count have no tile, and the others are
+// renumbered over the count, so that every XCD gets an equal contiguous
+// share of real tiles rather than the empty ones piling up on the last XCDs.
+template <bool GROUPED>
+__device__ __forceinline__ int tile_id(const KParams& p, int bm) {
+  if constexpr (!GROUPED) {
+    return xcd_remap(blockIdx.x, p.nblocks);
+  } else {
+    int total = 0;
+    for (int e = 0; e < p.G; ++e) {
+      const int64_t rows = (int64_t)p.offsets[e + 1] - p.offsets[e];
+      total += (int)((rows + bm - 1) / bm) * p.tiles_n;
+    }
+    if ((int)blockIdx.x >= total) return -1;
+    return xcd_remap(blockIdx.x, total);
+  }
+}
+
 // Logical id -> (tm, tn) in groups of kGroupM tile-rows.
 __device__ __forceinline__ void grouped_order(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
@@ -253,7 +274,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
   const int wn = wave & 1;
 
   // ---- tile decode
-  const int id = xcd_remap(blockIdx.x, p.nblocks);
+  const int id = tile_id<GROUPED>(p, kBM);
+  if (id < 0) return;
   const uint8_t* A = p.a;
   const uint8_t* B = p.b;
   const float* SB = p.sb;
@@ -720,7 +742,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
   const int wn = wave & 1;   // columns wn*kWN .. +kWN
 
   // ---- tile decode
-  const int id = xcd_remap(blockIdx.x, p.nblocks);
+  const int id = tile_id<GROUPED>(p, kBM);
+  if (id < 0) return;
   const uint8_t* A = p.a;
   const uint8_t* B = p.b;
   const float* SB = p.sb;
@@ -1006,6 +1029,309 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
   }
 }
 
+// ===========================================================================
+// Weight-streaming path (few rows per expert, as in MoE decode): the weights
+// are nearly all of the bytes and each is used by one row tile only, so the
+// kernel is bound by HBM, not by the matrix cores.  Tile 64 (M) x 32*SW (N);
+// SW waves, each 64 x 32 (two 32x32 row tiles, one column tile, so one B
+// scale block per wave).  The K groups stream through a ring of S LDS
+// stages, S - 1 of them in flight.  Every output element sees the same
+// operations in the same order as in gemm_rescale_kernel: the same K split
+// over lanes and steps, the same BF16 MFMAs, the same per-group rescale of D
+// with the 2^-64 floor, and the same epilogue; the results are identical.
+constexpr int kWBM = 64;  // rows per tile
+// grouped GEMMs with at most this many rows per expert on average stream
+constexpr int kStreamRowsPerExpert = 64;
+// 4 waves (128 columns) and a 3-stage ring: 72 KB of LDS, two workgroups
+// per CU.  Measured on 16 experts x ~32 tokens, 7168 -> 4096: 8 waves (one
+// workgroup per CU) with 3 or 4 stages, 4 waves with 2 or 4 stages, and 2
+// waves with 2 or 3 stages all stream slower.
+constexpr int kStreamWaves = 4;
+constexpr int kStreamStages = 3;
+constexpr int kStreamGroups = 1;  // K groups per stage
+
+// One stage holds KG consecutive K groups of the tile: rows of 128 KG bytes.
+template <int SW, int KG>
+struct __align__(16) StageW {
+  uint8_t a[kWBM * kBK * KG];
+  uint8_t b[32 * SW * kBK * KG];
+};
+
+// 16-byte chunk c of row r sits at chunk c ^ swz_w(r): with 128-byte rows as
+// in the tiled kernels, with 256-byte rows over all 16 chunks of the row, so
+// that 16 consecutive rows read at one logical chunk cover all 64 banks.
+template <int KG>
+__device__ __forceinline__ int swz_w(int row) {
+  return KG == 1 ? swz(row) : (row & 15);
+}
+
+// Workgroups per CU that the LDS ring allows (the register budget follows).
+template <int SW, int S, int KG>
+constexpr int stream_blocks_per_cu() {
+  return (160 * 1024) / (S * (int)sizeof(StageW<SW, KG>));
+}
+
+template <int CT, bool GROUPED, int SW, int S, int KG>
+__global__ __launch_bounds__(64 * SW, (stream_blocks_per_cu<SW, S, KG>())) void gemm_stream_kernel(KParams p) {
+  static_assert(S >= 2 && S <= 4, "two to four stages");
+  static_assert(KG == 1 || KG == 2, "one or two K groups per stage");
+  constexpr int kBNT = 32 * SW;
+  constexpr int kRow = kBK * KG;         // bytes per LDS row
+  constexpr int kRowsPerCopy = 1024 / kRow;
+  constexpr int kChunks = kRow / 16;     // 16-byte chunks per row
+  constexpr int kDmaA = kWBM * kRow / (1024 * SW);
+  constexpr int kDmaB = kBNT * kRow / (1024 * SW);
+  static_assert(kDmaA >= 1 && kDmaA * 1024 * SW == kWBM * kRow, "A copies per wave");
+  // vector-memory instructions per wave and stage: copies plus (2 + 1) scale loads per group
+  constexpr int kVmPerStage = kDmaA + kDmaB + 3 * KG;
+  using Stage = StageW<SW, KG>;
+  // One LDS object per stage (the K loop is unrolled by S), so the
+  // compiler's wait analysis sees which copies each read depends on.
+  __shared__ Stage st0;
+  __shared__ Stage st1;
+  __shared__ Stage st2;  // S >= 3
+  __shared__ Stage st3;  // S == 4
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // column tile of this wave
+
+  // ---- tile decode: logical id -> (expert, row tile, column tile), row tiles fastest
+  const int id = tile_id<GROUPED>(p, kWBM);
+  if (id < 0) return;
+  const uint8_t* A = p.a;
+  const uint8_t* B = p.b;
+  const float* SB = p.sb;
+  int64_t row_base = 0;
+  int rows_valid = 0;
+  int tn = 0;
+  if constexpr (GROUPED) {
+    int t = id;
+    int e = 0;
+    bool found = false;
+    for (; e < p.G; ++e) {
+      const int64_t seg0 = p.offsets[e];
+      const int64_t seg1 = p.offsets[e + 1];
+      const int tm_e = (int)((seg1 - seg0 + kWBM - 1) / kWBM);
+      const int cnt = tm_e * p.tiles_n;
+      if (t < cnt) {
+        const int tm = t % tm_e;
+        tn = t / tm_e;
+        row_base = seg0 + (int64_t)tm * kWBM;
+        const int64_t rem = seg1 - row_base;
+        rows_valid = rem < kWBM ? (int)rem : kWBM;
+        found = true;
+        break;
+      }
+      t -= cnt;
+    }
+    if (!found) return;
+    B += (int64_t)e * p.b_gs;
+    SB += (int64_t)e * p.sb_gs;
+  } else {
+    const int tiles_m = (int)((p.M + kWBM - 1) / kWBM);
+    const int tm = id % tiles_m;
+    tn = id / tiles_m;
+    row_base = (int64_t)tm * kWBM;
+    const int64_t rem = p.M - row_base;
+    rows_valid = rem < kWBM ? (int)rem : kWBM;
+  }
+  const int64_t n0 = p.n_base + (int64_t)tn * kBNT;
+  const int nkb = (int)(p.K / kBK);
+  const int nst = (nkb + KG - 1) / KG;  // stages of KG groups
+
+  // ---- copy sources: instruction i of wave w fills LDS rows (i * SW + w) * kRowsPerCopy .. + kRowsPerCopy
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kBNT * p.ldb));
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(p.a, 0u);
+  uint32_t a_off[kDmaA], b_off[kDmaB];
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = (i * SW + wave) * kRowsPerCopy + lane / kChunks;
+    const int ra = r < rows_valid ? r : rows_valid - 1;  // ragged M: repeat the last row
+    a_off[i] = (uint32_t)(ra * p.lda + (((lane % kChunks) ^ swz_w<KG>(r)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int r = (i * SW + wave) * kRowsPerCopy + lane / kChunks;
+    b_off[i] = (uint32_t)(r * p.ldb + (((lane % kChunks) ^ swz_w<KG>(r)) << 4));
+  }
+
+  // ---- scale sources: this lane's output row in row tile i is i*32 + lane % 32;
+  // the wave's 32 columns lie in B scale block (n0 + 32 wave) / 128
+  const int g = lane >> 5;
+  const int lr = lane & 31;
+  const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(p.sa + row_base * p.sa_ms, 0xFFFFFFFFu);
+  uint32_t sa_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = i * 32 + lr;
+    sa_off[i] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * p.sa_ms * 4);
+  }
+  const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(SB + ((n0 + 32 * wave) >> 7) * p.sb_ns, 0xFFFFFFFFu);
+  struct ScaleRegs {
+    float sa[KG][2];
+    float sb[KG];
+  };
+
+  // Stage sx's scales and copies (groups KG sx ..), all of them empty past
+  // the last group so that every stage issues the same instructions.  With
+  // KG = 2 and an odd group count the last stage copies 256 bytes per row
+  // of which the second half lies past K: the buffer range check returns
+  // zeros there, and that group is never computed.
+  auto issue = [&](int sx, Stage& Sx, ScaleRegs& sr) {
+#pragma unroll
+    for (int h = 0; h < KG; ++h) {
+      const int kb = KG * sx + h;
+      const bool live = kb < nkb;
+      const __amdgpu_buffer_rsrc_t rsa = live ? sa_rsrc : null_rsrc;
+      const __amdgpu_buffer_rsrc_t rsb = live ? sb_rsrc : null_rsrc;
+      const uint32_t ka = live ? (uint32_t)(kb * p.sa_ks * 4) : 0u;
+      const uint32_t kbo = live ? (uint32_t)(kb * p.sb_ks * 4) : 0u;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sr.sa[h][i] = load_f32(rsa, sa_off[i], ka);
+      sr.sb[h] = load_f32(rsb, 0u, kbo);
+    }
+    const bool live = sx < nst;
+    const uint32_t koff = live ? (uint32_t)sx * kRow : 0u;
+    const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : null_rsrc;
+    const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : null_rsrc;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) dma16(ra, a_off[i], koff, Sx.a + (i * SW + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) dma16(rb, b_off[i], koff, Sx.b + (i * SW + wave) * 1024);
+  };
+
+  v16f D[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) D[i][r] = 0.f;
+  // units of D per row tile: mc * 2^ec; emax: largest scale exponent taken
+  float mc[2] = {0.f, 0.f};
+  int ec[2] = {0, 0};
+  int emax[2] = {-(1 << 20), -(1 << 20)};
+
+  // K group h of the stage Sc: factors, rescale of D and the 8 K steps
+  auto compute = [&](int h, const Stage& Sc, const ScaleRegs& src) {
+    // factors of this group and the rescale of D (same arithmetic as gemm_rescale_kernel)
+    float rs[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float a = src.sa[h][i];
+      const float b = src.sb[h];
+      float m = __builtin_amdgcn_frexp_mantf(a) * __builtin_amdgcn_frexp_mantf(b);
+      int e = __builtin_amdgcn_frexp_expf(a) + __builtin_amdgcn_frexp_expf(b);
+      const bool low = a == 0.f || b == 0.f || e < emax[i] - kDropExp;
+      m = low ? 1.0f : m;
+      e = low ? emax[i] - kDropExp : e;
+      float r = __builtin_amdgcn_rcpf(m);
+      r = __builtin_fmaf(__builtin_fmaf(-m, r, 1.0f), r, r);
+      rs[i] = __builtin_amdgcn_ldexpf(mc[i] * r, ec[i] - e);
+      mc[i] = m;
+      ec[i] = e;
+      emax[i] = e > emax[i] ? e : emax[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) D[i][r] *= rs[i];
+    // lane half g holds K bytes 64 g .. 64 g + 63 of the group in four
+    // 16-byte chunks; step st multiplies bytes 64 g + 8 st .. + 7
+    uint4 ra[4][2], rb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = i * 32 + lr;
+        ra[c][i] = *reinterpret_cast<const uint4*>(Sc.a + row * kRow + (((8 * h + 4 * g + c) ^ swz_w<KG>(row)) << 4));
+      }
+      const int row = wave * 32 + lr;
+      rb[c] = *reinterpret_cast<const uint4*>(Sc.b + row * kRow + (((8 * h + 4 * g + c) ^ swz_w<KG>(row)) << 4));
+    }
+#pragma unroll
+    for (int stp = 0; stp < 8; ++stp) {
+      const int c = stp >> 1;
+      const bool hi = stp & 1;
+      const v8bf bf = hi ? fp8x8_to_bf16(rb[c].z, rb[c].w) : fp8x8_to_bf16(rb[c].x, rb[c].y);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const v8bf af = hi ? fp8x8_to_bf16(ra[c][i].z, ra[c][i].w) : fp8x8_to_bf16(ra[c][i].x, ra[c][i].y);
+        D[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, D[i], 0, 0, 0);
+      }
+    }
+  };
+
+  auto stage = [&](int sx, const Stage& Sc, Stage& Sr, const ScaleRegs& src, ScaleRegs& srr) {
+    // this stage's copies and scales are older than the S - 2 stages issued since
+    wait_vmcnt<(S - 2) * kVmPerStage>();
+    block_barrier();
+    issue(sx + S - 1, Sr, srr);  // into the stage every wave finished reading last time
+    compute(0, Sc, src);
+    if constexpr (KG == 2) {
+      if (KG * sx + 1 < nkb) compute(1, Sc, src);
+    }
+  };
+
+  ScaleRegs r0{}, r1{}, r2{}, r3{};
+  issue(0, st0, r0);
+  int sx = 0;
+  if constexpr (S == 2) {
+    for (; sx + 2 <= nst; sx += 2) {
+      stage(sx, st0, st1, r0, r1);
+      stage(sx + 1, st1, st0, r1, r0);
+    }
+    if (sx < nst) stage(sx, st0, st1, r0, r1);
+  } else if constexpr (S == 3) {
+    issue(1, st1, r1);
+    for (; sx + 3 <= nst; sx += 3) {
+      stage(sx, st0, st2, r0, r2);
+      stage(sx + 1, st1, st0, r1, r0);
+      stage(sx + 2, st2, st1, r2, r1);
+    }
+    if (sx < nst) stage(sx, st0, st2, r0, r2);
+    if (sx + 1 < nst) stage(sx + 1, st1, st0, r1, r0);
+  } else {
+    issue(1, st1, r1);
+    issue(2, st2, r2);
+    for (; sx + 4 <= nst; sx += 4) {
+      stage(sx, st0, st3, r0, r3);
+      stage(sx + 1, st1, st0, r1, r0);
+      stage(sx + 2, st2, st1, r2, r1);
+      stage(sx + 3, st3, st2, r3, r2);
+    }
+    if (sx < nst) stage(sx, st0, st3, r0, r3);
+    if (sx + 1 < nst) stage(sx + 1, st1, st0, r1, r0);
+    if (sx + 2 < nst) stage(sx + 2, st2, st1, r2, r1);
+  }
+  wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
+
+  // ---- epilogue: C = D * mc * 2^ec; lane holds row lr of row tile i,
+  // columns 8q + 4g .. +3 of the wave's 32
+  const bool vec = p.vec_store != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = i * 32 + lr;
+    if (row >= rows_valid) continue;
+    const int64_t grow = row_base + row;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t col = n0 + wave * 32 + 8 * q + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][4 * q + t] * mc[i], ec[i]);
+      store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+    }
+  }
+}
+
+template <int CT, bool GROUPED>
+hipError_t launch_stream(const KParams& kp, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_stream_kernel<CT, GROUPED, kStreamWaves, kStreamStages, kStreamGroups>), dim3(kp.nblocks),
+                     dim3(64 * kStreamWaves), 0, st, kp);
+  return hipGetLastError();
+}
+
 template <int CT, bool GROUPED, int JT>
 hipError_t launch_rescale(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((gemm_rescale_kernel<CT, GROUPED, JT>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
@@ -1094,6 +1420,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const bool grouped = g.G > 0;
   const int64_t tiles_m = grouped ? (g.M + kBM - 1) / kBM + g.G : (g.M + kBM - 1) / kBM;
   if (tiles_m == 0) return hipSuccess;
+  // Few rows per expert (or a dense M of at most one 64-row tile): the
+  // weight-streaming kernel on 64x128 tiles, two workgroups per CU.
+  if (mode == kModeExact && g.b_scale_mode == 0 &&
+      (grouped ? g.M <= kStreamRowsPerExpert * g.G : g.M <= kWBM)) {
+    const int64_t tm = grouped ? (g.M + kWBM - 1) / kWBM + g.G : (g.M + kWBM - 1) / kWBM;
+    kp.tiles_n = (int)(g.N / (32 * kStreamWaves));
+    kp.nblocks = (int)(tm * kp.tiles_n);
+    return g.c_type == 0 ? (grouped ? launch_stream<0, true>(kp, st) : launch_stream<0, false>(kp, st))
+                         : (grouped ? launch_stream<1, true>(kp, st) : launch_stream<1, false>(kp, st));
+  }
   // The default path with block scales runs the rescaled-accumulation
   // kernel on 256-column tiles and possibly a second launch of 192-column
   // tiles, the split that fills the CUs best (for a grouped GEMM tiles_m

@@ -135,6 +135,22 @@ def test_extreme_group_scales_per_row(N):
     _check_rows(c, oracle.gemm_blockscaled(qao, sao, qbo, sbo))
 
 
+def test_extreme_group_scales_per_row_streaming():
+    """The same rows through the weight-streaming kernel (dense calls of at
+    most 64 rows), on 256- and 128-column tiles."""
+    M, K = 256, 1024
+    x = _extreme_rows(M, K, 35)
+    qa, sa = T.quantize_1x128(f32_dev(x))
+    qao, sao = oracle.quantize_1x128(x)
+    for N in (512, 384):
+        w = (np.random.default_rng(36 + N).standard_normal((K, N)) * 0.02).astype(np.float32)
+        qb, sb = T.quantize_block(f32_dev(w))
+        qbo, sbo = oracle.quantize_128x128(w)
+        for r0 in range(0, M, 64):
+            c = host(T.gemm(qa[r0:r0 + 64], sa[r0:r0 + 64], qb, sb, out_dtype=torch.float32))
+            _check_rows(c, oracle.gemm_blockscaled(qao[r0:r0 + 64], sao[r0:r0 + 64], qbo, sbo))
+
+
 def test_extreme_group_scales_per_row_column_scales():
     """The same rows through the per-column-scale (wgrad) layout."""
     M, K, N = 256, 1024, 256
@@ -247,6 +263,33 @@ def grouped_case(counts, N, K, seed, what):
 
 def test_grouped_ragged_and_empty_experts():
     grouped_case([0, 5, 130, 0, 257, 1, 128], N=256, K=384, seed=30, what="grouped ragged")
+
+
+@pytest.mark.parametrize("N", [256, 384])
+def test_grouped_streaming_ragged_and_empty_experts(N):
+    # at most 64 rows per expert on average: the weight-streaming kernel, with
+    # experts of 0, 1, 64 (one full tile), 65 and 130 rows (ragged second and
+    # third tiles)
+    grouped_case([0, 5, 64, 65, 1, 0, 130, 33], N=N, K=640, seed=50, what="grouped streaming N=%d" % N)
+
+
+@pytest.mark.parametrize("N", [512, 384])
+def test_streaming_kernel_bitwise_equals_tiled_kernel(N):
+    """Rows computed by the weight-streaming kernel (a dense call of 64 rows,
+    a grouped call of 40) equal, bit for bit, the same rows of a 300-row
+    dense call on the 256-row tiles."""
+    M, K = 300, 768
+    a = rand_bits(M, K, seed=60, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=61, std=0.02)
+    qa, sa = T.quantize_1x128(bf16_dev(a))
+    qb, sb = T.quantize_block(bf16_dev(b))
+    for dt in (torch.float32, torch.bfloat16):
+        big = T.gemm(qa, sa, qb, sb, out_dtype=dt)
+        small = T.gemm(qa[100:164], sa[100:164], qb, sb, out_dtype=dt)
+        assert torch.equal(big[100:164], small)
+        offs = torch.tensor([0, 40], dtype=torch.int32, device=DEV)
+        grp = T.grouped_gemm(qa[7:47], sa[7:47], offs, qb.unsqueeze(0), sb.unsqueeze(0), out_dtype=dt)
+        assert torch.equal(big[7:47], grp)
 
 
 def test_grouped_single_expert_equals_dense():
