@@ -23,7 +23,7 @@ truncates inside its 8-product groups).  On this shape one GEMM call is two
 back-to-back launches of the same kernel, on 256- and on 192-column tiles
 (4096 and 3072 of the 7168 columns); the events bracket both.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 200]
     python bench.py --copy-calibration   # plain 1 GiB device copy, for the
                                          # HBM-counter scale factor
 """
@@ -50,8 +50,10 @@ GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_x1_amd", "csrc", "gemm.hip")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    # ~80 ms of untimed warmup: the clocks take tens of milliseconds to settle
+    # after the setup, and the first steps run up to 12% slower
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
