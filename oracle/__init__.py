@@ -48,6 +48,7 @@ from .gemm import (gemm_blockscaled, gemm_blockscaled_colscale,
                    grouped_gemm_blockscaled, wgrad, gemm_per_tensor,
                    bf16_rne_bits, bf16_bits_to_f64)
 from .metrics import rel_frob, max_rel
+from .limited_acc import limited_dot, gemm_limited_per_tensor
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "code_magnitudes",
@@ -58,5 +59,6 @@ __all__ = [
     "SCALE_AMAX", "SCALE_POW2",
     "gemm_blockscaled", "gemm_blockscaled_colscale",
     "grouped_gemm_blockscaled", "wgrad", "gemm_per_tensor",
+    "limited_dot", "gemm_limited_per_tensor",
     "bf16_rne_bits", "bf16_bits_to_f64", "rel_frob", "max_rel",
 ]

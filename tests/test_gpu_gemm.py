@@ -376,6 +376,16 @@ def test_workload3_full_size_sampled_and_naive_gap():
         "per-tensor no-promotion rel_frob=%.3e max_rel=%.3e" % (
             oracle.rel_frob(fine, truth), oracle.max_rel(fine, truth),
             oracle.rel_frob(naive, truth), oracle.max_rel(naive, truth)))
+    # context: the same per-tensor operands through the emulated 14-bit
+    # tensor-core accumulation the pages describe, on an 8 x 64 sub-block,
+    # against the exact product of the same E4M3 operands
+    er, ec = rows[:8], slice(0, 64)
+    for kk in (4096, 16384):
+        qa_k, qb_k = qao[er][:, :kk], qbo[:kk, ec]
+        exact = oracle.gemm_per_tensor(qa_k, s_a, qb_k, s_b)
+        emu = oracle.gemm_limited_per_tensor(qa_k, s_a, qb_k, s_b)
+        say("K=%d per-tensor E4M3, emulated 14-bit accumulation vs exact: rel_frob=%.3e max_rel=%.3e" % (
+            kk, oracle.rel_frob(emu, exact), oracle.max_rel(emu, exact)))
 
 
 def test_workload6_dgrad_full_size_sampled():
