@@ -26,7 +26,7 @@ FP8FG_BF16, FP8FG_F32, FP8FG_E4M3 = 0, 1, 2
 FP8FG_TILE_1x128, FP8FG_TILE_128x1 = 0, 1
 FP8FG_SCALE_AMAX, FP8FG_SCALE_POW2 = 0, 1
 FP8FG_BSCALE_BLOCK128, FP8FG_BSCALE_COL = 0, 1
-FP8FG_GEMM_DEFAULT, FP8FG_GEMM_NO_PROMOTION, FP8FG_GEMM_FP8_MFMA = 0, 1, 2
+FP8FG_GEMM_DEFAULT, FP8FG_GEMM_NO_PROMOTION, FP8FG_GEMM_FP8_MFMA, FP8FG_GEMM_E8M0_SCALES = 0, 1, 2, 4
 
 EXPORTED = ("fp8_quantize_rowtile", "fp8_quantize_block", "fp8_gemm_blockscaled",
             "fp8_grouped_gemm_blockscaled", "fp8fg_status_string")

@@ -59,7 +59,8 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
                       int b_scale_mode, void* c, int c_type, int64_t ldc, int flags) {
   if (b_scale_mode != FP8FG_BSCALE_BLOCK128 && b_scale_mode != FP8FG_BSCALE_COL) return FP8FG_EINVAL;
   if (c_type != FP8FG_BF16 && c_type != FP8FG_F32) return FP8FG_EINVAL;
-  if (flags & ~(FP8FG_GEMM_NO_PROMOTION | FP8FG_GEMM_FP8_MFMA)) return FP8FG_EINVAL;
+  if (flags & ~(FP8FG_GEMM_NO_PROMOTION | FP8FG_GEMM_FP8_MFMA | FP8FG_GEMM_E8M0_SCALES)) return FP8FG_EINVAL;
+  if ((flags & FP8FG_GEMM_E8M0_SCALES) && (flags & FP8FG_GEMM_NO_PROMOTION)) return FP8FG_EINVAL;
   if (M < 0 || N < 0 || K < 0 || lda < 0 || ldb < 0 || ldc < 0) return FP8FG_EINVAL;
   if (sa_ms < 0 || sa_ks < 0 || sb_ns < 0 || sb_ks < 0) return FP8FG_EINVAL;
   if ((flags & FP8FG_GEMM_NO_PROMOTION) && (sa_ks != 0 || sb_ks != 0)) return FP8FG_EINVAL;

@@ -27,7 +27,11 @@
 // FP8 paths (flags): MODE 1 forms P with one v_mfma_scale_f32_16x16x128_f8f6f4
 //   per 16x16 tile and K group (E8M0 operand scales = 1), then promotes as
 //   above; MODE 2 (no promotion) chains the FP8 MFMA over the whole K and
-//   applies per-tensor scales once -- the naive baseline.
+//   applies per-tensor scales once -- the naive baseline; MODE 3 gives each
+//   group's scales to the instruction as its E8M0 operand scales (their
+//   powers of two), so the products are dequantized inside the matrix unit
+//   and only a remaining factor, 1 for power-of-two scales, meets the FP32
+//   accumulate.
 //
 // Shared structure:
 //   * workgroup tile 256 (M) x 128 (N), eight waves in a 4x2 arrangement,
@@ -84,6 +88,7 @@ constexpr int kDmaPerGroup = kDmaA + kDmaB;
 constexpr int kModeExact = 0;     // BF16 MFMA partial sums
 constexpr int kModeFp8 = 1;       // FP8 MFMA partial sums, promoted
 constexpr int kModeFp8NoPromo = 2;
+constexpr int kModeFp8Mx = 3;     // FP8 MFMA applying the scales' powers of two as E8M0 operand scales
 
 struct __align__(16) Stage {
   uint8_t a[kBM * kBK];
@@ -596,7 +601,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
         bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
       float cv[4][4];
-      if constexpr (kColDma) {
+      float sbc[4];  // MODE 3, column scales: the column this lane supplies
+      if constexpr (kColDma && MODE == kModeFp8Mx) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sbc[j] = S.colsc[wave][j * 16 + fr];
+      } else if constexpr (kColDma) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float4 t = *reinterpret_cast<const float4*>(&S.colsc[wave][j * 16 + 4 * (lane >> 4)]);
@@ -617,6 +626,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
             if ((j * 4 + i) % 2 == 0 && (j * 4 + i) / 2 < kDmaPerGroup) issue_one(kb + 2, Nx, (j * 4 + i) / 2);
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 bf[j], af[i], acc[i][j], 0, 0, 0, kE8M0One, 0, kE8M0One);
+          }
+      } else if constexpr (MODE == kModeFp8Mx) {
+        // Each scale s splits into its power of two 2^(E - 127) -- E its
+        // exponent field, given to the instruction as an E8M0 operand scale
+        // -- and the rest f = s * 2^(127 - E), exactly 1 for a power of two
+        // (in [1, 2) otherwise, [0, 1) for 0 and denormals).  The lane that
+        // supplies B column wn*64 + 16 j + l % 16 (the instruction's first
+        // operand) gives that column's scale; the lane that supplies A row
+        // wm*64 + 16 i + l % 16 gives that row's.  The group's partial sum
+        // leaves the instruction scaled by the powers of two and is added to
+        // acc times fa * fb: for power-of-two scales a plain FP32 add.
+        int ea[4], eb[4];
+        float fa[4], fb[4];
+        auto split_scale = [](float sc, int& e, float& f) {
+          e = (int)((__float_as_uint(sc) >> 23) & 0xFFu);
+          f = __builtin_amdgcn_ldexpf(sc, 127 - e);
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_scale(sr.sa[i], ea[i], fa[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float sbj = sr.sb;
+          if constexpr (BMODE == 1) sbj = sbc[j];
+          split_scale(sbj, eb[j], fb[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if ((j * 4 + i) % 2 == 0 && (j * 4 + i) / 2 < kDmaPerGroup) issue_one(kb + 2, Nx, (j * 4 + i) / 2);
+            const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], zero, 0, 0, 0, eb[j], 0, ea[i]);
+            const float f = fa[i] * fb[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[r], f, acc[i][j][r]);
           }
       } else {
         if constexpr (!kColDma) {
@@ -1355,6 +1398,7 @@ hipError_t launch_mode(const KParams& kp, int mode, bool grouped, hipStream_t st
   switch (mode) {
     case kModeExact: return launch_grouped_or_dense<CT, BMODE, kModeExact>(kp, grouped, st);
     case kModeFp8: return launch_grouped_or_dense<CT, BMODE, kModeFp8>(kp, grouped, st);
+    case kModeFp8Mx: return launch_grouped_or_dense<CT, BMODE, kModeFp8Mx>(kp, grouped, st);
     default: return launch_grouped_or_dense<CT, BMODE, kModeFp8NoPromo>(kp, grouped, st);
   }
 }
@@ -1411,8 +1455,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   kp.b_gs = g.b_gs;
   kp.sb_gs = g.sb_gs;
   kp.G = (int)g.G;
-  const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION) ? kModeFp8NoPromo
-                   : (g.flags & FP8FG_GEMM_FP8_MFMA)   ? kModeFp8
+  const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION)  ? kModeFp8NoPromo
+                   : (g.flags & FP8FG_GEMM_E8M0_SCALES) ? kModeFp8Mx
+                   : (g.flags & FP8FG_GEMM_FP8_MFMA)    ? kModeFp8
                                                         : kModeExact;
   const int esize = g.c_type == 0 ? 2 : 4;
   kp.vec_store = (reinterpret_cast<uintptr_t>(g.c) % (4 * esize) == 0) && (g.ldc % 4 == 0);

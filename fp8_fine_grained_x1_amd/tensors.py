@@ -79,11 +79,12 @@ def quantize_block(w, pow2=False, transpose=True, stream=None):
 
 
 def gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16, col_scales=False, no_promotion=False,
-         fp8_mfma=False, out=None, stream=None):
+         fp8_mfma=False, e8m0_scales=False, out=None, stream=None):
     """col_scales=False: sb [K/128][N/128] block scales; True: sb [N][K/128].
     no_promotion: per-tensor scales (sa, sb hold one value each), whole-K
     FP8 matrix-core accumulation.  fp8_mfma: K-group partial sums from the
-    FP8 MFMA instead of the exact default path."""
+    FP8 MFMA instead of the exact default path.  e8m0_scales: the FP8 MFMA
+    applies the scales' powers of two as its E8M0 operand scales."""
     M, K = qa.shape
     N = qb.shape[0]
     c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qa.device)
@@ -97,18 +98,20 @@ def gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16, col_scales=False, no_promotio
             sb_ns, sb_ks = sb.stride(0), sb.stride(1)
         else:
             sb_ns, sb_ks = sb.stride(1), sb.stride(0)
-    flags = (B.FP8FG_GEMM_NO_PROMOTION if no_promotion else 0) | (B.FP8FG_GEMM_FP8_MFMA if fp8_mfma else 0)
+    flags = ((B.FP8FG_GEMM_NO_PROMOTION if no_promotion else 0) | (B.FP8FG_GEMM_FP8_MFMA if fp8_mfma else 0) |
+             (B.FP8FG_GEMM_E8M0_SCALES if e8m0_scales else 0))
     B.fp8_gemm_blockscaled(M, N, K, qa, qa.stride(0), sa, sa_ms, sa_ks, qb, qb.stride(0), sb,
                            sb_ns, sb_ks, mode, c, _CTYPE[c.dtype], c.stride(0), flags, stream)
     return c
 
 
-def grouped_gemm(qa, sa, offsets, qb, sb, out_dtype=torch.bfloat16, out=None, stream=None):
+def grouped_gemm(qa, sa, offsets, qb, sb, out_dtype=torch.bfloat16, out=None, stream=None,
+                 flags=B.FP8FG_GEMM_DEFAULT):
     M, K = qa.shape
     G, N, _ = qb.shape
     c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qa.device)
     B.fp8_grouped_gemm_blockscaled(G, offsets, M, N, K, qa, qa.stride(0), sa, sa.stride(0),
                                    sa.stride(1), qb, qb.stride(1), qb.stride(0), sb, sb.stride(2),
                                    sb.stride(1), sb.stride(0), c, _CTYPE[c.dtype], c.stride(0),
-                                   B.FP8FG_GEMM_DEFAULT, stream)
+                                   flags, stream)
     return c

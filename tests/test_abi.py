@@ -136,8 +136,11 @@ def test_block_validation(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(b_scale_mode=3), B.FP8FG_EINVAL),
     (dict(c_type=B.FP8FG_E4M3), B.FP8FG_EINVAL),
-    (dict(flags=4), B.FP8FG_EINVAL),
+    (dict(flags=8), B.FP8FG_EINVAL),
     (dict(flags=B.FP8FG_GEMM_FP8_MFMA, c=None), B.FP8FG_EINVAL),   # flag accepted, then null c
+    (dict(flags=B.FP8FG_GEMM_E8M0_SCALES, c=None), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_E8M0_SCALES | B.FP8FG_GEMM_FP8_MFMA, c=None), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_E8M0_SCALES | B.FP8FG_GEMM_NO_PROMOTION, sa_ks=0, sb_ks=0), B.FP8FG_EINVAL),
     (dict(M=-1), B.FP8FG_EINVAL),
     (dict(sa_ms=-2), B.FP8FG_EINVAL),
     (dict(flags=B.FP8FG_GEMM_NO_PROMOTION), B.FP8FG_EINVAL),   # per-K scales with no promotion

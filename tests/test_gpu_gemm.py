@@ -236,6 +236,78 @@ def test_fp8_mfma_flag_within_group_bound():
     assert np.all(err <= bound)
 
 
+@pytest.mark.parametrize("N", [256, 384])
+def test_e8m0_scales_equal_promoted_fp8_mfma_for_pow2(N):
+    """E8M0 path with power-of-two scales: the instruction applies the scales
+    exactly, so the result equals the promoted FP8-MFMA path bit for bit
+    (acc + sa sb P rounded once either way), and both stay within the FP8
+    MFMA's group-truncation bound of the oracle."""
+    M, K = 200, 640
+    a = rand_bits(M, K, seed=70, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=71, std=0.02)
+    qa, sa = T.quantize_1x128(bf16_dev(a), pow2=True)
+    qb, sb = T.quantize_block(bf16_dev(b), pow2=True)
+    for dt in (torch.float32, torch.bfloat16):
+        mx = T.gemm(qa, sa, qb, sb, out_dtype=dt, e8m0_scales=True)
+        pr = T.gemm(qa, sa, qb, sb, out_dtype=dt, fp8_mfma=True)
+        assert torch.equal(mx, pr)
+    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, e8m0_scales=True)).astype(np.float64)
+    qao, sao = oracle.quantize_1x128(f32(a), oracle.SCALE_POW2)
+    qbo, sbo = oracle.quantize_128x128(f32(b), oracle.SCALE_POW2)
+    ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+    bound = fp8_mfma_bound(qao, sao, qbo, np.repeat(sbo, 128, axis=1))
+    err = np.abs(c32 - ref)
+    say("e8m0 N=%d: rel_frob=%.3e; max err/bound=%.3f" % (N, oracle.rel_frob(c32, ref), np.max(err / bound)))
+    assert np.all(err <= bound)
+
+
+def test_e8m0_scales_any_scale_within_bound():
+    """Scales that are not powers of two: the instruction takes their powers
+    of two and the rest multiplies the partial sum, so the result is still
+    the block-scaled product within the FP8 MFMA bound."""
+    M, N, K = 96, 256, 512
+    a = rand_bits(M, K, seed=72, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=73, std=0.02)
+    qa, sa = T.quantize_1x128(bf16_dev(a))
+    qb, sb = T.quantize_block(bf16_dev(b))
+    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, e8m0_scales=True)).astype(np.float64)
+    qao, sao = oracle.quantize_1x128(f32(a))
+    qbo, sbo = oracle.quantize_128x128(f32(b))
+    ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+    bound = fp8_mfma_bound(qao, sao, qbo, np.repeat(sbo, 128, axis=1))
+    err = np.abs(c32 - ref)
+    say("e8m0 amax scales: rel_frob=%.3e; max err/bound=%.3f" % (oracle.rel_frob(c32, ref), np.max(err / bound)))
+    assert np.all(err <= bound)
+
+
+def test_e8m0_scales_column_scales_and_grouped():
+    # per-column (wgrad) scales, power of two: equal to the promoted FP8 path
+    T_, F, Nn = 512, 256, 384
+    x = rand_bits(T_, F, seed=74)
+    dy = rand_bits(T_, Nn, seed=75)
+    qx, sx = T.quantize_128x1(bf16_dev(x), pow2=True)
+    qd, sd = T.quantize_128x1(bf16_dev(dy), pow2=True)
+    mx = T.gemm(qx, sx, qd, sd, out_dtype=torch.float32, col_scales=True, e8m0_scales=True)
+    pr = T.gemm(qx, sx, qd, sd, out_dtype=torch.float32, col_scales=True, fp8_mfma=True)
+    assert torch.equal(mx, pr)
+    # grouped, ragged and empty experts: equal to the promoted FP8 path
+    counts = np.array([0, 37, 300, 1, 0, 129])
+    off = workloads.moe_offsets(counts)
+    M, N, K = int(counts.sum()), 256, 384
+    a = rand_bits(M, K, seed=76)
+    qa, sa = T.quantize_1x128(bf16_dev(a), pow2=True)
+    qb = torch.empty((len(counts), N, K), dtype=torch.uint8, device=DEV)
+    sb = torch.empty((len(counts), K // 128, N // 128), dtype=torch.float32, device=DEV)
+    for e in range(len(counts)):
+        q, s_ = T.quantize_block(bf16_dev(rand_bits(K, N, seed=77 + e, std=0.02)), pow2=True)
+        qb[e].copy_(q)
+        sb[e].copy_(s_)
+    offs = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    gm = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32, flags=B.FP8FG_GEMM_E8M0_SCALES)
+    gp = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32, flags=B.FP8FG_GEMM_FP8_MFMA)
+    assert torch.equal(gm, gp)
+
+
 # ---------------------------------------------------------------- grouped
 def grouped_case(counts, N, K, seed, what):
     counts = np.asarray(counts, np.int64)
