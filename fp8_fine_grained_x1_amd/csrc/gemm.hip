@@ -16,24 +16,28 @@
 // no promotion interval can remove it (relative Frobenius error ~5e-5 on
 // the reference workloads).  The BF16 MFMA has no such loss.  Hence:
 //
-// default path (MODE 0, exact partial sums):
-//   * the FP8 tiles stay FP8 in HBM and LDS (half the bytes of BF16);
-//   * each wave converts its fragments FP8 -> BF16 in registers with
-//     v_cvt_scalef32_pk_bf16_fp8 (scale 1.0: exact, every E4M3 value is a
-//     BF16 value) and runs v_mfma_f32_32x32x16_bf16, chaining the 8
-//     16-wide K steps of a K group in one accumulator P;
-//   * promotion acc = fma(P, sa(m,kb) * sb(kb,n), acc) on the VALU, once per
-//     output element and K group.
-// FP8 paths (flags): MODE 1 forms P with one v_mfma_scale_f32_16x16x128_f8f6f4
-//   per 16x16 tile and K group (E8M0 operand scales = 1), then promotes as
-//   above; MODE 2 (no promotion) chains the FP8 MFMA over the whole K and
-//   applies per-tensor scales once -- the naive baseline; MODE 3 gives each
-//   group's scales to the instruction as its E8M0 operand scales (their
-//   powers of two), so the products are dequantized inside the matrix unit
-//   and only a remaining factor, 1 for power-of-two scales, meets the FP32
-//   accumulate.
+// Kernels (which one runs is decided on the host from the arguments):
+//   * gemm_rescale_kernel -- the default path with 128x128 B block scales:
+//     exact partial sums (the FP8 fragments are converted to BF16 in
+//     registers with v_cvt_scalef32_pk_bf16_fp8, scale 1.0, which is exact,
+//     and multiplied with v_mfma_f32_32x32x16_bf16) accumulated in units of
+//     the current K group's scale, the accumulator rescaled once per group;
+//     256 x 256 and 256 x 192 tiles (described before the kernel);
+//   * gemm_stream_kernel -- the same arithmetic for few rows per expert
+//     (MoE decode) or a dense M <= 64: 64 x 128 tiles, weight streaming;
+//   * gemm_blockscaled_kernel -- promotion of separate K-group partial sums:
+//     MODE 0 (exact, as above) for per-column B scales and N = 128; the FP8
+//     paths behind flags: MODE 1 forms P with one
+//     v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 tile and K group (E8M0
+//     operand scales = 1) and promotes acc = fma(P, sa * sb, acc); MODE 2
+//     (no promotion) chains the FP8 MFMA over the whole K and applies
+//     per-tensor scales once -- the naive baseline; MODE 3 gives each group's
+//     scales to the instruction as its E8M0 operand scales (their powers of
+//     two), so the products are dequantized inside the matrix unit and only
+//     a remaining factor, 1 for power-of-two scales, meets the FP32
+//     accumulate.
 //
-// Shared structure:
+// gemm_blockscaled_kernel structure:
 //   * workgroup tile 256 (M) x 128 (N), eight waves in a 4x2 arrangement,
 //     each wave a 64x64 sub-tile; one workgroup per CU;
 //   * A and B tiles (256 + 128 rows x 128 K bytes = 48 KB per K group) move
@@ -53,9 +57,9 @@
 //   * workgroup ids are remapped so that consecutive tiles run on the same
 //     XCD (each XCD has its own L2), and tiles are ordered in groups of
 //     M-tiles so that co-resident workgroups share A and B panels.
-// Grouped GEMM: the same tile kernel; a workgroup's linear tile id is
-// resolved against the device-side expert offsets (expert-major order), so
-// ragged and empty experts need no host synchronization.
+// Grouped GEMM: the same kernels; a workgroup's linear tile id is resolved
+// against the device-side expert offsets (expert-major order), so ragged and
+// empty experts need no host synchronization.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

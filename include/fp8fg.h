@@ -141,10 +141,18 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *   C[m][n] = sum_kb  sa(m, kb) * sb(kb, n) * P_kb[m][n],
  *   P_kb[m][n] = sum_{k = 128 kb}^{128 kb + 127} dec(a[m * lda + k]) * dec(b[n * ldb + k])
  *
- *   Default path: each P_kb is summed exactly-faithfully (the FP8 operands are
+ *   Default path: the products of each P_kb are exact (the FP8 operands are
  *   converted exactly to BF16 in registers and multiplied on the BF16 matrix
- *   cores with FP32 accumulation), then promoted into the FP32 accumulator with
- *   its two scales (one FMA per output element and K group).
+ *   cores) and added in FP32; the group's two scales are applied to the FP32
+ *   accumulator once per output element and K group (with 128x128 B block
+ *   scales the accumulator is kept in units of the current group's scale and
+ *   rescaled at each group; a group whose scale lies more than 2^64 below
+ *   the largest taken so far for that element is added in units of 2^-64 of
+ *   it).  Kernels, tiles and launch counts are chosen from the arguments;
+ *   with block scales and N >= 256 every choice gives the same result bit
+ *   for bit (so a row's result does not depend on M or on the expert
+ *   counts); N = 128 and per-column scales use a kernel that promotes
+ *   separate group sums, whose rounding differs within the same accuracy.
  *
  *   a : E4M3 [M][K] (K contiguous), sa(m, kb) = sa[m * sa_ms + kb * sa_ks].
  *   b : E4M3 [N][K] (K contiguous -- the transposed weight),
