@@ -25,6 +25,12 @@
 //     256 x 256 and 256 x 192 tiles (described before the kernel);
 //   * gemm_stream_kernel -- the same arithmetic for few rows per expert
 //     (MoE decode) or a dense M <= 64: 64 x 128 tiles, weight streaming;
+//   * gemm_mx_kernel -- the E8M0-scale flag with block scales and N a
+//     multiple of 256: 256 x 256 tiles of v_mfma_scale_f32_32x32x64_f8f6f4,
+//     the FP8 operands unconverted, the scales' powers of two as the
+//     instruction's operand scales; while the leftover factors are 1 the
+//     accumulator is chained through the instruction (described before the
+//     kernel);
 //   * gemm_blockscaled_kernel -- promotion of separate K-group partial sums:
 //     MODE 0 (exact, as above) for per-column B scales and N = 128; the FP8
 //     paths behind flags: MODE 1 forms P with one
@@ -1384,6 +1390,272 @@ hipError_t launch_stream(const KParams& kp, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ===========================================================================
+// E8M0-scale path on 256 x 256 tiles (128x128 B block scales, N % 256 == 0):
+// the FP8 operands go to v_mfma_scale_f32_32x32x64_f8f6f4 unconverted, with
+// each group's scales split as in MODE 3 of gemm_blockscaled_kernel -- the
+// power of two as the instruction's E8M0 operand scale, the rest f (1 for
+// power-of-two scales) applied to the partial sum.  When every f of a wave
+// is 1 the group's products accumulate in the instruction itself (no VALU
+// work per element); otherwise each 64-byte K slice's partial sum is formed
+// apart and added as acc = fma(P, f, acc).  Eight waves of 64 x 128 (2 x 4
+// tiles of 32 x 32), two LDS stages, copies one group ahead, as in
+// gemm_rescale_kernel.  Against MODE 3's 256 x 128 tiles this halves the
+// LDS bytes read per MFMA flop and, chained, drops the VALU promotion.
+//
+// Lane l of an MFMA supplies row l % 32 of its operand and 32 of the 64 K
+// bytes (half l / 32); A and B fragments use the same split, so every
+// product pairs matching K elements whatever order the instruction sums
+// them in, and the lanes of one row share that row's scale.
+template <int CT, bool GROUPED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(KParams p) {
+  constexpr int kBNT = 256;
+  constexpr int kDmaA = kBM / (8 * kWaves);
+  constexpr int kDmaB = kBNT / (8 * kWaves);
+  __shared__ Stage2<4> stage0;
+  __shared__ Stage2<4> stage1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1;  // rows wm*64 .. +64
+  const int wn = wave & 1;   // columns wn*128 .. +128
+
+  const int id = tile_id<GROUPED>(p, kBM);
+  if (id < 0) return;
+  const uint8_t* A = p.a;
+  const uint8_t* B = p.b;
+  const float* SB = p.sb;
+  int64_t row_base = 0;
+  int rows_valid = 0;
+  int tn = 0;
+  if constexpr (GROUPED) {
+    int t = id;
+    int e = 0;
+    bool found = false;
+    for (; e < p.G; ++e) {
+      const int64_t seg0 = p.offsets[e];
+      const int64_t seg1 = p.offsets[e + 1];
+      const int tm_e = (int)((seg1 - seg0 + kBM - 1) / kBM);
+      const int cnt = tm_e * p.tiles_n;
+      if (t < cnt) {
+        int tm;
+        grouped_order(t, tm_e, p.tiles_n, tm, tn);
+        row_base = seg0 + (int64_t)tm * kBM;
+        const int64_t rem = seg1 - row_base;
+        rows_valid = rem < kBM ? (int)rem : kBM;
+        found = true;
+        break;
+      }
+      t -= cnt;
+    }
+    if (!found) return;
+    B += (int64_t)e * p.b_gs;
+    SB += (int64_t)e * p.sb_gs;
+  } else {
+    const int tiles_m = (int)((p.M + kBM - 1) / kBM);
+    int tm;
+    grouped_order(id, tiles_m, p.tiles_n, tm, tn);
+    row_base = (int64_t)tm * kBM;
+    const int64_t rem = p.M - row_base;
+    rows_valid = rem < kBM ? (int)rem : kBM;
+  }
+  const int64_t n0 = (int64_t)tn * kBNT;
+  const int nkb = (int)(p.K / kBK);
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kBNT * p.ldb));
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(p.a, 0u);
+  uint32_t a_off[kDmaA], b_off[kDmaB];
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    const int ra = r < rows_valid ? r : rows_valid - 1;
+    a_off[i] = (uint32_t)(ra * p.lda + (((lane & 7) ^ swz(r)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    b_off[i] = (uint32_t)(r * p.ldb + (((lane & 7) ^ swz(r)) << 4));
+  }
+  auto issue = [&](int kb, Stage2<4>& S) {
+    const bool live = kb < nkb;
+    const uint32_t koff = live ? (uint32_t)kb * kBK : 0u;
+    const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : null_rsrc;
+    const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : null_rsrc;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) dma16(ra, a_off[i], koff, S.a + (i * kWaves + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) dma16(rb, b_off[i], koff, S.b + (i * kWaves + wave) * 1024);
+  };
+
+  // scales: rows wm*64 + i*32 + lane % 32; the wave's 128 columns are one B block
+  const int g = lane >> 5;
+  const int lr = lane & 31;
+  const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(p.sa + row_base * p.sa_ms, 0xFFFFFFFFu);
+  uint32_t sa_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wm * 64 + i * 32 + lr;
+    sa_off[i] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * p.sa_ms * 4);
+  }
+  const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(SB + ((n0 + wn * 128) >> 7) * p.sb_ns, 0xFFFFFFFFu);
+  struct ScaleRegs {
+    float sa[2];
+    float sb;
+  };
+  auto load_scales = [&](int kb, ScaleRegs& s) {
+    const bool live = kb < nkb;
+    const __amdgpu_buffer_rsrc_t ra = live ? sa_rsrc : null_rsrc;
+    const uint32_t ka = live ? (uint32_t)(kb * p.sa_ks * 4) : 0u;
+    const uint32_t kbo = live ? (uint32_t)(kb * p.sb_ks * 4) : 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s.sa[i] = load_f32(ra, sa_off[i], ka);
+    s.sb = load_f32(live ? sb_rsrc : null_rsrc, 0u, kbo);
+  };
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // A group's scales split for the scaled MFMA: E8M0 bytes and the factors
+  // left over (f = 1 for power-of-two scales), and whether every f of the
+  // wave is 1.
+  struct Split {
+    int ea[2], eb;
+    float fa[2];
+    bool unit;
+  };
+  auto split = [&](const ScaleRegs& sr) {
+    Split sp;
+    bool one = true;
+    const float sb = sr.sb;
+    sp.eb = (int)((__float_as_uint(sb) >> 23) & 0xFFu);
+    const float fb = __builtin_amdgcn_ldexpf(sb, 127 - sp.eb);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      sp.ea[i] = (int)((__float_as_uint(sr.sa[i]) >> 23) & 0xFFu);
+      sp.fa[i] = __builtin_amdgcn_ldexpf(sr.sa[i], 127 - sp.ea[i]) * fb;
+      one = one && sp.fa[i] == 1.0f;
+    }
+    sp.unit = __builtin_amdgcn_ballot_w64(!one) == 0;
+    return sp;
+  };
+
+  // LDS fragment offsets: rows wm*64 + i*32 + lr (A) and wn*128 + j*32 + lr
+  // (B) all have swz(row) = swz(lr); lane half g reads chunks 4s + 2g, +1.
+  const int sw = swz(lr);
+  uint32_t f_off[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) f_off[s][h] = (uint32_t)(lr * 128 + (((4 * s + 2 * g + h) ^ sw) << 4));
+  auto frag = [&](const uint8_t* base, uint32_t row0, int s) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row0 * 128 + f_off[s][0]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row0 * 128 + f_off[s][1]);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  // One K group: wait for its stage, load the scales of group kb + 2 into
+  // lsr and start the copies of group kb + 1 (scales first, so that using
+  // them waits on no copy), then the MFMAs of its two 64-byte K slices.  The
+  // stages are passed statically: with a stage picked at run time the
+  // compiler cannot tell the copies' LDS target from the stage being read
+  // and drains the copies before the reads.
+  auto group = [&](bool chain, int kb, const Stage2<4>& S, Stage2<4>& Nx, const Split& sp, ScaleRegs& lsr) {
+    wait_vmcnt<0>();
+    block_barrier();
+    load_scales(kb + 2, lsr);
+    issue(kb + 1, Nx);
+    const v16f zero = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      v8i af[2], bf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = frag(S.a, wm * 64 + i * 32, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = frag(S.b, wn * 128 + j * 32, s);
+      if (chain) {
+        // every factor of the wave is 1: the products accumulate in the instruction
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, sp.eb, 0,
+                                                                         sp.ea[i]);
+      } else {
+        // general factors: the slice's partial sum apart, then acc = fma(P, f, acc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const v16f P =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], zero, 0, 0, 0, sp.eb, 0, sp.ea[i]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[r], sp.fa[i], acc[i][j][r]);
+            __builtin_amdgcn_sched_barrier(0);  // one partial sum live at a time
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one slice's fragments live at a time
+    }
+  };
+
+  ScaleRegs sr0{}, sr1{};
+  load_scales(0, sr0);
+  load_scales(1, sr1);
+  issue(0, stage0);
+  Split sp0 = split(sr0), sp1 = split(sr1);
+  // Pairs of groups run chained while every factor of the wave in both is 1;
+  // from the first pair with another factor on, the wave takes the general
+  // form to the end of K.  The decision is taken only at the head of a pair
+  // (an exit between the two groups lets the register allocator place the
+  // accumulators differently on the two paths and spill); every wave meets
+  // one barrier per group on either path.
+  int kb = 0;
+  for (; kb + 2 <= nkb && sp0.unit && sp1.unit; kb += 2) {
+    group(true, kb, stage0, stage1, sp0, sr0);
+    group(true, kb + 1, stage1, stage0, sp1, sr1);
+    sp0 = split(sr0);
+    sp1 = split(sr1);
+  }
+  for (; kb + 2 <= nkb; kb += 2) {
+    group(false, kb, stage0, stage1, sp0, sr0);
+    group(false, kb + 1, stage1, stage0, sp1, sr1);
+    sp0 = split(sr0);
+    sp1 = split(sr1);
+  }
+  if (kb < nkb) group(false, kb, stage0, stage1, sp0, sr0);
+  wait_vmcnt<0>();
+
+  // epilogue: lane holds row lr of row tile i, columns 8q + 4g .. +3 of column tile j
+  const bool vec = p.vec_store != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = wm * 64 + i * 32 + lr;
+    if (row >= rows_valid) continue;
+    const int64_t grow = row_base + row;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t];
+        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+      }
+  }
+}
+
+template <int CT, bool GROUPED>
+hipError_t launch_mx(const KParams& kp, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_mx_kernel<CT, GROUPED>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
+  return hipGetLastError();
+}
+
 template <int CT, bool GROUPED, int JT>
 hipError_t launch_rescale(const KParams& kp, hipStream_t st) {
   hipLaunchKernelGGL((gemm_rescale_kernel<CT, GROUPED, JT>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
@@ -1474,6 +1746,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const bool grouped = g.G > 0;
   const int64_t tiles_m = grouped ? (g.M + kBM - 1) / kBM + g.G : (g.M + kBM - 1) / kBM;
   if (tiles_m == 0) return hipSuccess;
+  // E8M0 scales with block scales and N % 256 == 0: 256 x 256 tiles.
+  if (mode == kModeFp8Mx && g.b_scale_mode == 0 && g.N % 256 == 0) {
+    kp.tiles_n = (int)(g.N / 256);
+    kp.nblocks = (int)(tiles_m * kp.tiles_n);
+    return g.c_type == 0 ? (grouped ? launch_mx<0, true>(kp, st) : launch_mx<0, false>(kp, st))
+                         : (grouped ? launch_mx<1, true>(kp, st) : launch_mx<1, false>(kp, st));
+  }
   // Few rows per expert (or a dense M of at most one 64-row tile): the
   // weight-streaming kernel on 64x128 tiles, two workgroups per CU.
   if (mode == kModeExact && g.b_scale_mode == 0 &&

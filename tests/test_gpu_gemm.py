@@ -236,12 +236,13 @@ def test_fp8_mfma_flag_within_group_bound():
     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("N", [256, 384])
+@pytest.mark.parametrize("N", [128, 384])
 def test_e8m0_scales_equal_promoted_fp8_mfma_for_pow2(N):
-    """E8M0 path with power-of-two scales: the instruction applies the scales
-    exactly, so the result equals the promoted FP8-MFMA path bit for bit
-    (acc + sa sb P rounded once either way), and both stay within the FP8
-    MFMA's group-truncation bound of the oracle."""
+    """E8M0 path on 128-column tiles (N not a multiple of 256) with
+    power-of-two scales: the instruction applies the scales exactly, so the
+    result equals the promoted FP8-MFMA path bit for bit (acc + sa sb P
+    rounded once either way), and both stay within the FP8 MFMA's
+    group-truncation bound of the oracle."""
     M, K = 200, 640
     a = rand_bits(M, K, seed=70, outliers=0.01, mult=50)
     b = rand_bits(K, N, seed=71, std=0.02)
@@ -290,10 +291,11 @@ def test_e8m0_scales_column_scales_and_grouped():
     mx = T.gemm(qx, sx, qd, sd, out_dtype=torch.float32, col_scales=True, e8m0_scales=True)
     pr = T.gemm(qx, sx, qd, sd, out_dtype=torch.float32, col_scales=True, fp8_mfma=True)
     assert torch.equal(mx, pr)
-    # grouped, ragged and empty experts: equal to the promoted FP8 path
+    # grouped, ragged and empty experts, 128-column tiles: equal to the
+    # promoted FP8 path
     counts = np.array([0, 37, 300, 1, 0, 129])
     off = workloads.moe_offsets(counts)
-    M, N, K = int(counts.sum()), 256, 384
+    M, N, K = int(counts.sum()), 384, 384
     a = rand_bits(M, K, seed=76)
     qa, sa = T.quantize_1x128(bf16_dev(a), pow2=True)
     qb = torch.empty((len(counts), N, K), dtype=torch.uint8, device=DEV)
@@ -306,6 +308,87 @@ def test_e8m0_scales_column_scales_and_grouped():
     gm = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32, flags=B.FP8FG_GEMM_E8M0_SCALES)
     gp = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32, flags=B.FP8FG_GEMM_FP8_MFMA)
     assert torch.equal(gm, gp)
+
+
+def e8m0_wide_check(qao, sao, qbo, sbo, what, offsets=None, qbs=None, sbs=None):
+    """E8M0 path on 256-column tiles (N a multiple of 256): FP32 result
+    within the FP8 MFMA bound of the oracle for the scales as given, BF16
+    result = RNE of the FP32 one.  Operands come from the oracle's arrays."""
+    qa = torch.from_numpy(np.ascontiguousarray(qao)).to(DEV)
+    sa = f32_dev(sao)
+    if offsets is None:
+        qb = torch.from_numpy(np.ascontiguousarray(qbo.T)).to(DEV)
+        sb = f32_dev(sbo)
+        run = lambda dt: T.gemm(qa, sa, qb, sb, out_dtype=dt, e8m0_scales=True)
+        ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
+        bound = fp8_mfma_bound(qao, sao, qbo, np.repeat(sbo, 128, axis=1))
+    else:
+        qb = torch.from_numpy(np.stack([np.ascontiguousarray(q.T) for q in qbs])).to(DEV)
+        sb = f32_dev(np.stack(sbs))
+        offs = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
+        run = lambda dt: T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=dt, flags=B.FP8FG_GEMM_E8M0_SCALES)
+        ref = oracle.grouped_gemm_blockscaled(qao, sao, offsets, qbs, sbs)
+        bound = np.zeros_like(ref)
+        for e in range(len(qbs)):
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 > r0:
+                bound[r0:r1] = fp8_mfma_bound(qao[r0:r1], sao[r0:r1], qbs[e], np.repeat(sbs[e], 128, axis=1))
+    c32 = host(run(torch.float32)).astype(np.float64)
+    c16 = host(run(torch.bfloat16))
+    err = np.abs(c32 - ref)
+    say("%s: rel_frob=%.3e; max err/bound=%.3f" % (what, oracle.rel_frob(c32, ref), np.max(err / bound)))
+    assert np.all(err <= bound)
+    assert np.array_equal(c16, oracle.bf16_rne_bits(c32.astype(np.float32)))
+    return c32
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 256, 640), (300, 512, 1024), (64, 256, 128)])
+def test_e8m0_wide_tiles_pow2_within_bound(M, N, K):
+    # an odd number of K groups (the last one alone), an even number, and a
+    # single group; ragged row tiles
+    a = rand_bits(M, K, seed=80 + M, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=81 + N, std=0.02)
+    qao, sao = oracle.quantize_1x128(f32(a), oracle.SCALE_POW2)
+    qbo, sbo = oracle.quantize_128x128(f32(b), oracle.SCALE_POW2)
+    e8m0_wide_check(qao, sao, qbo, sbo, "e8m0 wide pow2 %dx%dx%d" % (M, N, K))
+
+
+def test_e8m0_wide_tiles_mixed_scales_within_bound():
+    """Power-of-two scales with some made general part way along K: the rows
+    of one 32-row tile from group 3 on, one B block's scale in group 5.  The
+    waves holding them leave the chained form for the general one at the
+    next pair of groups; the others stay chained.  The oracle takes the same
+    scales."""
+    M, N, K = 256, 512, 1024
+    a = rand_bits(M, K, seed=90, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=91, std=0.02)
+    qao, sao = oracle.quantize_1x128(f32(a), oracle.SCALE_POW2)
+    qbo, sbo = oracle.quantize_128x128(f32(b), oracle.SCALE_POW2)
+    sao = sao.astype(np.float32).copy()
+    sbo = sbo.astype(np.float32).copy()
+    sao[32:64, 3:] *= np.float32(1.5)
+    sao[200, 0] *= np.float32(0.75)
+    sbo[5, 2] *= np.float32(1.25)
+    e8m0_wide_check(qao, sao, qbo, sbo, "e8m0 wide mixed scales")
+
+
+def test_e8m0_wide_tiles_amax_scales_within_bound():
+    M, N, K = 160, 256, 768
+    a = rand_bits(M, K, seed=92, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=93, std=0.02)
+    qao, sao = oracle.quantize_1x128(f32(a))
+    qbo, sbo = oracle.quantize_128x128(f32(b))
+    e8m0_wide_check(qao, sao, qbo, sbo, "e8m0 wide amax scales")
+
+
+def test_e8m0_wide_tiles_grouped_ragged_and_empty_experts():
+    counts = np.array([0, 37, 300, 1, 0, 129, 256])
+    off = workloads.moe_offsets(counts)
+    M, N, K = int(counts.sum()), 256, 384
+    qao, sao = oracle.quantize_1x128(f32(rand_bits(M, K, seed=94)), oracle.SCALE_POW2)
+    qbs, sbs = zip(*[oracle.quantize_128x128(f32(rand_bits(K, N, seed=95 + e, std=0.02)), oracle.SCALE_POW2)
+                     for e in range(len(counts))])
+    e8m0_wide_check(qao, sao, None, None, "e8m0 wide grouped", offsets=off, qbs=qbs, sbs=sbs)
 
 
 # ---------------------------------------------------------------- grouped
