@@ -310,6 +310,10 @@ def main():
                                        1, o["N"] // 128, (o["K"] // 128) * (o["N"] // 128), o["c"],
                                        B.FP8FG_BF16, o["N"], B.FP8FG_GEMM_DEFAULT, stream)
 
+    g4 = grouped_setup(4)
+    up_ms = timed(lambda: grouped(g4))
+    up_flops = 2.0 * g4["M"] * g4["N"] * g4["K"]
+    del g4
     g7 = grouped_setup(7)
     dn_ms = timed(lambda: grouped(g7))
     dn_flops = 2.0 * g7["M"] * g7["N"] * g7["K"]
@@ -324,6 +328,28 @@ def main():
     dc_desc = "G=%d, %d tokens (%d-%d per expert), K=%d -> N=%d" % (
         g8["G"], g8["M"], min(g8["counts"]), max(g8["counts"]), g8["K"], g8["N"])
     del g8
+    # Long-K dense GEMM (1024 x 4096 x 16384: 128 promotions per output).
+    from fp8_fine_grained_x1_amd import tensors as T
+    w3 = workloads.WORKLOADS[3]
+    d3 = workloads.workload_inputs(3)
+    qa3, sa3 = T.quantize_1x128(to_dev(d3["A"]))
+    qb3, sb3 = T.quantize_block(to_dev(d3["B"]))
+    c3 = torch.empty((w3["M"], w3["N"]), dtype=torch.bfloat16, device=dev)
+    lk_ms = timed(lambda: T.gemm(qa3, sa3, qb3, sb3, out=c3))
+    lk_flops = 2.0 * w3["M"] * w3["N"] * w3["K"]
+    del d3, qa3, sa3, qb3, sb3, c3
+    # Weight gradient dW [F][N] = X^T dY over T = 8192 tokens: X and dY
+    # quantized 1x128, requantized to 128x1 tiles (transposed, per-column
+    # scales along the token axis), FP32 out.
+    w5 = workloads.WORKLOADS[5]
+    d5 = workloads.workload_inputs(5)
+    qx5, sx5 = T.requantize_128x1(*T.quantize_1x128(to_dev(d5["X"])))
+    qd5, sd5 = T.requantize_128x1(*T.quantize_1x128(to_dev(d5["dY"])))
+    c5 = torch.empty((w5["F"], w5["N"]), dtype=torch.float32, device=dev)
+    wg_ms = timed(lambda: T.gemm(qx5, sx5, qd5, sd5, out=c5, col_scales=True))
+    wg_flops = 2.0 * w5["F"] * w5["N"] * w5["T"]
+    del d5, qx5, sx5, qd5, sd5, c5
+
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     gemm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
@@ -380,6 +406,17 @@ def main():
             "fp8_gemm_blockscaled dgrad dX = dY.W^T, 4096x7168x7168 (outside the step)": {
                 "ms": round(dg_ms, 4), "TFLOP/s": round(tflops(flops, dg_ms), 1),
                 "frac_bf16_peak": round(tflops(flops, dg_ms) / PEAK_BF16_TFLOPS, 4)},
+            "fp8_gemm_blockscaled long K 1024x4096x16384 (outside the step)": {
+                "ms": round(lk_ms, 4), "TFLOP/s": round(tflops(lk_flops, lk_ms), 1),
+                "frac_bf16_peak": round(tflops(lk_flops, lk_ms) / PEAK_BF16_TFLOPS, 4)},
+            "fp8_gemm_blockscaled wgrad dW = X^T.dY 7168x4096, 8192 tokens, 128x1 column scales, "
+            "f32 out (outside the step)": {
+                "ms": round(wg_ms, 4), "TFLOP/s": round(tflops(wg_flops, wg_ms), 1),
+                "frac_bf16_peak": round(tflops(wg_flops, wg_ms) / PEAK_BF16_TFLOPS, 4)},
+            "fp8_grouped_gemm_blockscaled MoE up-projection G=8, 16384 tokens, K=7168 -> N=4096, "
+            "pow2 activation scales (outside the step)": {
+                "ms": round(up_ms, 4), "TFLOP/s": round(tflops(up_flops, up_ms), 1),
+                "frac_bf16_peak": round(tflops(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4)},
             "fp8_grouped_gemm_blockscaled MoE down-projection G=8, 16384 tokens, K=4096 -> N=7168, "
             "pow2 activation scales (outside the step)": {
                 "ms": round(dn_ms, 4), "TFLOP/s": round(tflops(dn_flops, dn_ms), 1),

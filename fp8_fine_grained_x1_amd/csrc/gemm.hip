@@ -68,6 +68,8 @@
 // empty experts need no host synchronization.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "device_common.h"
 #include "fp8fg.h"
@@ -1715,6 +1717,19 @@ ColumnPlan plan_columns(int64_t tiles_m, int64_t N, int cus) {
   return best;
 }
 
+// Override of the choice between the 64x128 and the 256-row tiles of the
+// exact path, read from the environment at each call (for tests and
+// tuning; every choice gives the same result): FP8FG_GEMM_TILES=wide or
+// =narrow, anything else (or unset) chooses from the shape.
+enum class TileChoice { kAuto, kWide, kNarrow };
+static TileChoice tile_choice() {
+  const char* v = getenv("FP8FG_GEMM_TILES");
+  if (v == nullptr) return TileChoice::kAuto;
+  if (strcmp(v, "wide") == 0) return TileChoice::kWide;
+  if (strcmp(v, "narrow") == 0) return TileChoice::kNarrow;
+  return TileChoice::kAuto;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   KParams kp;
   kp.M = g.M;
@@ -1753,10 +1768,20 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     return g.c_type == 0 ? (grouped ? launch_mx<0, true>(kp, st) : launch_mx<0, false>(kp, st))
                          : (grouped ? launch_mx<1, true>(kp, st) : launch_mx<1, false>(kp, st));
   }
-  // Few rows per expert (or a dense M of at most one 64-row tile): the
-  // weight-streaming kernel on 64x128 tiles, two workgroups per CU.
-  if (mode == kModeExact && g.b_scale_mode == 0 &&
-      (grouped ? g.M <= kStreamRowsPerExpert * g.G : g.M <= kWBM)) {
+  // Exact path with block scales: the weight-streaming kernel on 64x128
+  // tiles, two workgroups per CU, for few rows per expert, a dense M of at
+  // most one 64-row tile, or a dense grid of 256x256 tiles that would fill
+  // at most half of the CUs (small M x N with a long K: per CU the 64x128
+  // tiles deliver about half the rate of the 256x256 ones, so they win once
+  // they keep at least twice the CUs busy).  Both tile shapes give every
+  // output element bit for bit the same value.
+  const TileChoice tc = tile_choice();
+  const int64_t wide_tiles = tiles_m * ((g.N + 255) / 256);
+  const bool narrow = tc == TileChoice::kNarrow ? true
+                      : tc == TileChoice::kWide ? false
+                      : grouped                  ? g.M <= kStreamRowsPerExpert * g.G
+                                                 : (g.M <= kWBM || wide_tiles * 2 <= device_cu_count());
+  if (mode == kModeExact && g.b_scale_mode == 0 && narrow) {
     const int64_t tm = grouped ? (g.M + kWBM - 1) / kWBM + g.G : (g.M + kWBM - 1) / kWBM;
     kp.tiles_n = (int)(g.N / (32 * kStreamWaves));
     kp.nblocks = (int)(tm * kp.tiles_n);

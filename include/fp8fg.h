@@ -153,6 +153,11 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *   for bit (so a row's result does not depend on M or on the expert
  *   counts); N = 128 and per-column scales use a kernel that promotes
  *   separate group sums, whose rounding differs within the same accuracy.
+ *   Small grids (few 256x256 tiles for the compute units, as with a small
+ *   M x N and a long K) run on 64x128 tiles.  The environment variable
+ *   FP8FG_GEMM_TILES=wide or =narrow, read at each call, fixes the choice
+ *   between the 256-row and the 64x128 tiles of this path (for tests and
+ *   tuning).
  *
  *   a : E4M3 [M][K] (K contiguous), sa(m, kb) = sa[m * sa_ms + kb * sa_ks].
  *   b : E4M3 [N][K] (K contiguous -- the transposed weight),

@@ -17,7 +17,7 @@ from fp8_fine_grained_x1_amd import binding as B
 from fp8_fine_grained_x1_amd import tensors as T
 from fp8_fine_grained_x1_amd import workloads
 from gpu_util import (DEV, bf16_dev, check_bf16_output, check_gemm, f32, f32_dev, fp8_mfma_bound,
-                      host, say, workload)
+                      host, say, tiles, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,13 +43,23 @@ def dense_case(a_bits, b_bits, a_pow2=False, b_pow2=False, what="", scale_layout
     qbo, sbo = oracle.quantize_128x128(f32(b_bits), rb)
     assert np.array_equal(host(qa), qao) and np.array_equal(host(sa), sao)
     assert np.array_equal(host(qb), qbo.T) and np.array_equal(host(sb), sbo)
-    c32 = T.gemm(qa, sa, qb, sb, out_dtype=torch.float32)
-    c16 = T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16)
     ref = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
-    h32 = host(c32)
-    check_gemm(h32, ref, what)
-    check_bf16_output(host(c16), h32, ref)
-    return h32, ref
+    # both tile shapes of the exact path and the automatic choice, each
+    # against the oracle; from N = 256 on they agree bit for bit (at N = 128
+    # the 256-row choice promotes separate group sums)
+    outs = {}
+    for choice in ("wide", "narrow", None):
+        with tiles(choice):
+            h32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+            h16 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16))
+        check_gemm(h32, ref, "%s (%s tiles)" % (what, choice or "chosen"))
+        check_bf16_output(h16, h32, ref)
+        outs[choice] = (h32, h16)
+    if qb.shape[0] >= 256:
+        for choice in ("narrow", None):
+            assert np.array_equal(outs[choice][0], outs["wide"][0]), choice
+            assert np.array_equal(outs[choice][1], outs["wide"][1]), choice
+    return outs[None][0], ref
 
 
 @pytest.mark.parametrize("scale_layout", ["group_major", "row_major"])
@@ -82,10 +92,12 @@ def test_identity_weights_bit_exact():
     qa, sa = T.quantize_1x128(bf16_dev(a))
     eye = torch.eye(K, dtype=torch.bfloat16, device=DEV)
     qb, sb = T.quantize_block(eye, pow2=True, transpose=True)
-    c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
     qao, sao = oracle.quantize_1x128(f32(a))
     expect = (oracle.decode(qao).astype(np.float32) * np.repeat(sao, 128, axis=1)).astype(np.float32)
-    assert np.array_equal(c32, expect)
+    for choice in ("wide", "narrow"):
+        with tiles(choice):
+            c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+        assert np.array_equal(c32, expect), choice
 
 
 def _extreme_rows(M, K, seed):
@@ -131,7 +143,8 @@ def test_extreme_group_scales_per_row(N):
     qao, sao = oracle.quantize_1x128(x)
     qbo, sbo = oracle.quantize_128x128(w)
     assert np.array_equal(host(qa), qao) and np.array_equal(host(sa), sao)
-    c = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+    with tiles("wide"):
+        c = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
     _check_rows(c, oracle.gemm_blockscaled(qao, sao, qbo, sbo))
 
 
@@ -172,6 +185,12 @@ def test_strided_output_and_guard_bands():
     b = rand_bits(K, N, seed=9, std=0.02)
     qa, sa = T.quantize_1x128(bf16_dev(a))
     qb, sb = T.quantize_block(bf16_dev(b))
+    for choice in ("wide", "narrow"):
+        with tiles(choice):
+            strided_output_case(qa, sa, qb, sb, a, b, M, N, choice)
+
+
+def strided_output_case(qa, sa, qb, sb, a, b, M, N, choice):
     cbuf = torch.full((M + 2, N + 64), 12345.0, dtype=torch.float32, device=DEV)
     c = cbuf[1:M + 1, 32:32 + N]
     T.gemm(qa, sa, qb, sb, out=c)
@@ -180,7 +199,7 @@ def test_strided_output_and_guard_bands():
     mask[1:M + 1, 32:32 + N] = False
     assert np.all(hb[mask] == 12345.0)
     ref = oracle.gemm_blockscaled(*oracle.quantize_1x128(f32(a)), *oracle.quantize_128x128(f32(b)))
-    check_gemm(hb[1:M + 1, 32:32 + N], ref, "strided")
+    check_gemm(hb[1:M + 1, 32:32 + N], ref, "strided, %s tiles" % choice)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 256), (384, 512, 640)])
@@ -439,7 +458,8 @@ def test_streaming_kernel_bitwise_equals_tiled_kernel(N):
     qa, sa = T.quantize_1x128(bf16_dev(a))
     qb, sb = T.quantize_block(bf16_dev(b))
     for dt in (torch.float32, torch.bfloat16):
-        big = T.gemm(qa, sa, qb, sb, out_dtype=dt)
+        with tiles("wide"):
+            big = T.gemm(qa, sa, qb, sb, out_dtype=dt)
         small = T.gemm(qa[100:164], sa[100:164], qb, sb, out_dtype=dt)
         assert torch.equal(big[100:164], small)
         offs = torch.tensor([0, 40], dtype=torch.int32, device=DEV)
@@ -482,8 +502,13 @@ def dense_full_size(w, pow2_a=False):
     say("workload %d: M=%d N=%d K=%d" % (w, M, N, K))
     qa, sa = T.quantize_1x128(bf16_dev(a_bits), pow2=pow2_a)
     qb, sb = T.quantize_block(bf16_dev(b_bits))
+    # the tiles bench.py's launch takes (chosen from the shape) ...
     c32 = T.gemm(qa, sa, qb, sb, out_dtype=torch.float32)
     c16 = T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16)
+    # ... equal, over the whole output, those of both forced choices
+    for choice in ("wide", "narrow"):
+        with tiles(choice):
+            assert torch.equal(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32), c32), choice
     rows = sample_rows(M, w)
     qao, sao = oracle.quantize_1x128(f32(a_bits[rows]))
     idx = torch.from_numpy(rows).to(DEV)
