@@ -28,9 +28,9 @@
 //   * gemm_mx_kernel -- the E8M0-scale flag with block scales and N a
 //     multiple of 256: 256 x 256 tiles of v_mfma_scale_f32_32x32x64_f8f6f4,
 //     the FP8 operands unconverted, the scales' powers of two as the
-//     instruction's operand scales; while the leftover factors are 1 the
-//     accumulator is chained through the instruction (described before the
-//     kernel);
+//     instruction's operand scales, the accumulator chained through the
+//     instruction and kept in units of the leftover factors (described
+//     before the kernel);
 //   * gemm_blockscaled_kernel -- promotion of separate K-group partial sums:
 //     MODE 0 (exact, as above) for per-column B scales and N = 128; the FP8
 //     paths behind flags: MODE 1 forms P with one
@@ -1397,13 +1397,15 @@ hipError_t launch_stream(const KParams& kp, hipStream_t st) {
 // the FP8 operands go to v_mfma_scale_f32_32x32x64_f8f6f4 unconverted, with
 // each group's scales split as in MODE 3 of gemm_blockscaled_kernel -- the
 // power of two as the instruction's E8M0 operand scale, the rest f (1 for
-// power-of-two scales) applied to the partial sum.  When every f of a wave
-// is 1 the group's products accumulate in the instruction itself (no VALU
-// work per element); otherwise each 64-byte K slice's partial sum is formed
-// apart and added as acc = fma(P, f, acc).  Eight waves of 64 x 128 (2 x 4
-// tiles of 32 x 32), two LDS stages, copies one group ahead, as in
-// gemm_rescale_kernel.  Against MODE 3's 256 x 128 tiles this halves the
-// LDS bytes read per MFMA flop and, chained, drops the VALU promotion.
+// power-of-two scales) applied in FP32.  The products always accumulate in
+// the instruction itself; the accumulator holds D / u, u the f of the
+// current group per lane and row tile, and is multiplied by u / f where a
+// group's f differs (the scheme of gemm_rescale_kernel, with the powers of
+// two left to the instruction; D = acc * u at the end).  Power-of-two
+// scales need no multiply at all.  Eight waves of 64 x 128 (2 x 4 tiles of
+// 32 x 32), two LDS stages, copies one group ahead, as in
+// gemm_rescale_kernel.  Against MODE 3's 256 x 128 tiles this halves the LDS
+// bytes read per MFMA flop and replaces its per-group FMA promotion.
 //
 // Lane l of an MFMA supplies row l % 32 of its operand and 32 of the 64 K
 // bytes (half l / 32); A and B fragments use the same split, so every
@@ -1523,27 +1525,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(KParams p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // A group's scales split for the scaled MFMA: E8M0 bytes and the factors
-  // left over (f = 1 for power-of-two scales), and whether every f of the
-  // wave is 1.
+  // The accumulator holds D / u[i], one unit per lane and row tile i: the
+  // leftover factor f of the last group (1 at the start, and throughout for
+  // power-of-two scales).  A group's split gives the instruction's E8M0
+  // bytes and r = u / f, the rescale that brings the accumulator to the
+  // group's units before its products are chained in (none when f = u).
+  // Scales are positive (an E8M0 scale has no zero), so f > 0.  The splits
+  // run two groups ahead; those of the groups past the end of K (whose
+  // scale loads read nothing) leave u as it is.
+  float u[2] = {1.f, 1.f};
   struct Split {
     int ea[2], eb;
-    float fa[2];
-    bool unit;
+    float r[2];
+    bool rescale;  // some r of the wave differs from 1
   };
-  auto split = [&](const ScaleRegs& sr) {
+  auto split = [&](const ScaleRegs& sr, int kb) {
     Split sp;
-    bool one = true;
+    bool resc = false;
+    const bool live = kb < nkb;
     const float sb = sr.sb;
     sp.eb = (int)((__float_as_uint(sb) >> 23) & 0xFFu);
     const float fb = __builtin_amdgcn_ldexpf(sb, 127 - sp.eb);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       sp.ea[i] = (int)((__float_as_uint(sr.sa[i]) >> 23) & 0xFFu);
-      sp.fa[i] = __builtin_amdgcn_ldexpf(sr.sa[i], 127 - sp.ea[i]) * fb;
-      one = one && sp.fa[i] == 1.0f;
+      const float f = __builtin_amdgcn_ldexpf(sr.sa[i], 127 - sp.ea[i]) * fb;
+      // u / f, exactly 1 when f = u (a reciprocal refined by one Newton step
+      // otherwise; its last-bit error is far below the FP8 MFMA's)
+      float rf = __builtin_amdgcn_rcpf(f);
+      rf = __builtin_fmaf(__builtin_fmaf(-f, rf, 1.0f), rf, rf);
+      sp.r[i] = f == u[i] ? 1.0f : u[i] * rf;
+      u[i] = live ? f : u[i];
+      resc = resc || sp.r[i] != 1.f;
     }
-    sp.unit = __builtin_amdgcn_ballot_w64(!one) == 0;
+    sp.rescale = __builtin_amdgcn_ballot_w64(resc) != 0;
     return sp;
   };
 
@@ -1561,78 +1576,78 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(KParams p) {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
 
-  // One K group: wait for its stage, load the scales of group kb + 2 into
-  // lsr and start the copies of group kb + 1 (scales first, so that using
-  // them waits on no copy), then the MFMAs of its two 64-byte K slices.  The
-  // stages are passed statically: with a stage picked at run time the
-  // compiler cannot tell the copies' LDS target from the stage being read
-  // and drains the copies before the reads.
-  auto group = [&](bool chain, int kb, const Stage2<4>& S, Stage2<4>& Nx, const Split& sp, ScaleRegs& lsr) {
+  // One K group: wait for its stage, read its first slice's fragments,
+  // bring the accumulator to the group's units, load the scales of group
+  // kb + 2 into lsr and start the copies of group kb + 1 (scales first, so
+  // that using them waits on no copy), then chain the MFMAs of its two
+  // 64-byte K slices.  The stages are passed statically: with a stage picked
+  // at run time the compiler cannot tell the copies' LDS target from the
+  // stage being read and drains the copies before the reads.
+  auto group = [&](bool units, int kb, const Stage2<4>& S, Stage2<4>& Nx, const Split& sp, ScaleRegs& lsr) {
     wait_vmcnt<0>();
     block_barrier();
-    load_scales(kb + 2, lsr);
-    issue(kb + 1, Nx);
-    const v16f zero = {};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i af[2], bf[4];
+    v8i af[2], bf[4];
+    auto read = [&](int s) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) af[i] = frag(S.a, wm * 64 + i * 32, s);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bf[j] = frag(S.b, wn * 128 + j * 32, s);
-      if (chain) {
-        // every factor of the wave is 1: the products accumulate in the instruction
+    };
+    auto mfmas = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, sp.eb, 0,
-                                                                         sp.ea[i]);
-      } else {
-        // general factors: the slice's partial sum apart, then acc = fma(P, f, acc)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const v16f P =
-                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], zero, 0, 0, 0, sp.eb, 0, sp.ea[i]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[r], sp.fa[i], acc[i][j][r]);
-            __builtin_amdgcn_sched_barrier(0);  // one partial sum live at a time
-          }
-      }
+        for (int i = 0; i < 2; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, sp.eb, 0,
+                                                                       sp.ea[i]);
       __builtin_amdgcn_sched_barrier(0);  // one slice's fragments live at a time
+    };
+    read(0);  // in flight during the rescale
+    if (units && sp.rescale) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= sp.r[i];
     }
+    // issued here, in the block of the first MFMAs, so that they interleave
+    load_scales(kb + 2, lsr);
+    issue(kb + 1, Nx);
+    mfmas();
+    read(1);
+    mfmas();
   };
 
   ScaleRegs sr0{}, sr1{};
   load_scales(0, sr0);
   load_scales(1, sr1);
   issue(0, stage0);
-  Split sp0 = split(sr0), sp1 = split(sr1);
-  // Pairs of groups run chained while every factor of the wave in both is 1;
-  // from the first pair with another factor on, the wave takes the general
-  // form to the end of K.  The decision is taken only at the head of a pair
-  // (an exit between the two groups lets the register allocator place the
-  // accumulators differently on the two paths and spill); every wave meets
-  // one barrier per group on either path.
+  Split sp0 = split(sr0, 0);
+  Split sp1 = split(sr1, 1);
+  // Pairs of groups with nothing to rescale (power-of-two scales) run in a
+  // loop without the rescale code: its branch, even untaken, splits the
+  // group's block and costs about 6% here.  From the first pair with a
+  // rescale on, the wave runs the other loop to the end of K; every wave
+  // meets one barrier per group on either path.
   int kb = 0;
-  for (; kb + 2 <= nkb && sp0.unit && sp1.unit; kb += 2) {
-    group(true, kb, stage0, stage1, sp0, sr0);
-    group(true, kb + 1, stage1, stage0, sp1, sr1);
-    sp0 = split(sr0);
-    sp1 = split(sr1);
-  }
-  for (; kb + 2 <= nkb; kb += 2) {
+  for (; kb + 2 <= nkb && !sp0.rescale && !sp1.rescale; kb += 2) {
     group(false, kb, stage0, stage1, sp0, sr0);
     group(false, kb + 1, stage1, stage0, sp1, sr1);
-    sp0 = split(sr0);
-    sp1 = split(sr1);
+    sp0 = split(sr0, kb + 2);
+    sp1 = split(sr1, kb + 3);
   }
-  if (kb < nkb) group(false, kb, stage0, stage1, sp0, sr0);
+  for (; kb + 2 <= nkb; kb += 2) {
+    group(true, kb, stage0, stage1, sp0, sr0);
+    group(true, kb + 1, stage1, stage0, sp1, sr1);
+    sp0 = split(sr0, kb + 2);
+    sp1 = split(sr1, kb + 3);
+  }
+  if (kb < nkb) group(true, kb, stage0, stage1, sp0, sr0);
   wait_vmcnt<0>();
 
-  // epilogue: lane holds row lr of row tile i, columns 8q + 4g .. +3 of column tile j
+  // epilogue: lane holds row lr of row tile i, columns 8q + 4g .. +3 of
+  // column tile j; D = acc * u
   const bool vec = p.vec_store != 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1646,7 +1661,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(KParams p) {
         const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
         float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t];
+        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * u[i];
         store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
       }
   }

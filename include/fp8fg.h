@@ -178,17 +178,19 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *       passage on exponents shared within small groups): the FP8 MFMA
  *       dequantizes: each scale's power of two 2^(E - 127), E its exponent
  *       field, is the instruction's E8M0 operand scale, and the rest
- *       s * 2^(127 - E) -- exactly 1 when s is a power of two, as
- *       FP8FG_SCALE_POW2 produces -- multiplies the group's partial sum as it
- *       is added to the FP32 accumulator.  With block scales and N a
- *       multiple of 256 the kernel runs on 256x256 tiles and, over each
- *       pair of K groups where every leftover factor of a 64-row by
- *       128-column part of the tile is 1, adds the products into the
- *       accumulator inside the instruction (no separate group sum): the
- *       rounding then differs from FP8_MFMA's within the same bound.
- *       Otherwise (N not a multiple of 256, per-column scales) power-of-two
- *       scales give FP8_MFMA's result bit for bit.  Scales must be finite
- *       and non-negative.  Not combinable with NO_PROMOTION (FP8FG_EINVAL).
+ *       f = s * 2^(127 - E) -- exactly 1 when s is a power of two, as
+ *       FP8FG_SCALE_POW2 produces -- is applied in FP32.  With block scales
+ *       and N a multiple of 256 the kernel runs on 256x256 tiles and adds
+ *       the products into the accumulator inside the instruction; the
+ *       accumulator is kept in units of the current group's f per row and
+ *       rescaled by one multiply where f changes (never for power-of-two
+ *       scales), as the default path does with whole scales.  Its rounding
+ *       then differs from FP8_MFMA's within the same bound.  Otherwise (N
+ *       not a multiple of 256, per-column scales) each group's partial sum
+ *       is multiplied by f as it is added, and power-of-two scales give
+ *       FP8_MFMA's result bit for bit.  Scales must be finite and positive
+ *       (an E8M0 scale has no zero; the quantizers' scales are at least
+ *       2^-126).  Not combinable with NO_PROMOTION (FP8FG_EINVAL).
  *   Alignment: a, b 16-byte aligned, lda and ldb multiples of 16; c aligned
  *   to its element; scales 4-byte aligned.  (c 16-byte aligned with ldc a
  *   multiple of 4 lets the kernel store 4 outputs per instruction.)
