@@ -432,6 +432,12 @@ def grouped_case(counts, N, K, seed, what):
     ref = oracle.grouped_gemm_blockscaled(qao, sao, off, qbs, sbs)
     check_gemm(c32, ref, what)
     check_bf16_output(c16, c32, ref)
+    if N >= 256:
+        # both tile shapes of the exact path give the same bits
+        for choice in ("wide", "narrow"):
+            with tiles(choice):
+                assert np.array_equal(host(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32)),
+                                      c32), choice
     return qa, sa, offs, qb, sb, c32
 
 
@@ -611,6 +617,9 @@ def grouped_full_size(w):
     offs = torch.from_numpy(off.astype(np.int32)).to(DEV)
     c32 = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32)
     c16 = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.bfloat16)
+    # the other tile shape of the exact path gives the same bits
+    with tiles("narrow" if M > 64 * G else "wide"):
+        assert torch.equal(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32), c32)
     rng = np.random.default_rng(44)
     for e in range(G):
         r0, r1 = int(off[e]), int(off[e + 1])
