@@ -22,6 +22,9 @@ converted exactly to BF16 in registers, because the FP8 matrix instruction
 truncates inside its 8-product groups).  On this shape one GEMM call is two
 back-to-back launches of the same kernel, on 256- and on 192-column tiles
 (4096 and 3072 of the 7168 columns); the events bracket both.
+`hbm_copy_context` times a plain 1 GiB device copy in the same run: the HBM
+rate a pure stream reaches here, beside which the quantizers' fractions of
+the published 8 TB/s are to be read.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 200]
     python bench.py --copy-calibration   # plain 1 GiB device copy, for the
@@ -359,6 +362,13 @@ def main():
     wg_flops = 2.0 * w5["F"] * w5["N"] * w5["T"]
     del d5, qx5, sx5, qd5, sd5, c5
 
+    # Context for the HBM fractions: a plain 1 GiB device-to-device copy (the
+    # runtime's copy kernel) in the same run, read + write bytes per time.
+    cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    cp_dst = torch.empty_like(cp_src)
+    cp_ms = timed(lambda: cp_dst.copy_(cp_src), reps=10)
+    del cp_src, cp_dst
+
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     gemm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
@@ -439,6 +449,9 @@ def main():
                 "frac_hbm": round(gbs(dc_bytes, dc_ms) / PEAK_HBM_GBS, 3),
                 "TFLOP/s": round(tflops(dc_flops, dc_ms), 1)},
         },
+        "hbm_copy_context": {
+            "1 GiB device copy GB/s (read + write)": round(gbs(2 * (1 << 30), cp_ms), 1),
+            "frac_hbm": round(gbs(2 * (1 << 30), cp_ms) / PEAK_HBM_GBS, 3)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile()},
