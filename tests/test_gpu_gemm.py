@@ -391,13 +391,15 @@ def test_e8m0_wide_tiles_mixed_scales_within_bound():
     e8m0_wide_check(qao, sao, qbo, sbo, "e8m0 wide mixed scales")
 
 
-def test_e8m0_wide_tiles_amax_scales_within_bound():
-    M, N, K = 160, 256, 768
-    a = rand_bits(M, K, seed=92, outliers=0.01, mult=50)
-    b = rand_bits(K, N, seed=93, std=0.02)
+@pytest.mark.parametrize("M,N,K", [(160, 256, 768), (100, 512, 640), (64, 256, 128)])
+def test_e8m0_wide_tiles_amax_scales_within_bound(M, N, K):
+    # every group rescales the accumulator: an even and an odd number of K
+    # groups, and a single one
+    a = rand_bits(M, K, seed=92 + K, outliers=0.01, mult=50)
+    b = rand_bits(K, N, seed=93 + N, std=0.02)
     qao, sao = oracle.quantize_1x128(f32(a))
     qbo, sbo = oracle.quantize_128x128(f32(b))
-    e8m0_wide_check(qao, sao, qbo, sbo, "e8m0 wide amax scales")
+    e8m0_wide_check(qao, sao, qbo, sbo, "e8m0 wide amax scales %dx%dx%d" % (M, N, K))
 
 
 def test_e8m0_wide_tiles_grouped_ragged_and_empty_experts():
