@@ -29,6 +29,8 @@ the published 8 TB/s are to be read.
     python bench.py [--gpus 1] [--steps 100] [--warmup 200]
     python bench.py --copy-calibration   # plain 1 GiB device copy, for the
                                          # HBM-counter scale factor
+    python bench.py --kernel gemm|e8m0   # one GEMM kernel alone on the same
+                                         # operands, for counter profiles
 """
 
 import argparse
@@ -59,6 +61,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel", choices=["gemm", "e8m0"],
+                   help="run only this GEMM on the workload's operands (default path, or the "
+                        "E8M0-scale path on power-of-two operands), --steps times after "
+                        "--warmup, and print its mean time (for counter profiles)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (counter calibration)")
     return p.parse_args()
@@ -132,6 +138,38 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
+def kernel_only(args, M, N, K, st, stream, B):
+    """One GEMM kernel alone, repeated: the default path on the step's amax
+    operands, or the E8M0-scale path on power-of-two operands."""
+    import torch
+    G = K // 128
+    pow2 = args.kernel == "e8m0"
+    rule = B.FP8FG_SCALE_POW2 if pow2 else B.FP8FG_SCALE_AMAX
+    B.fp8_quantize_rowtile(st["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128, rule,
+                           st["qa"], K, st["sa"], 1, M, stream)
+    B.fp8_quantize_block(st["b"], B.FP8FG_BF16, K, N, N, rule, 1, st["qb"], K, st["sb"], N // 128, 1,
+                         stream)
+    flags = B.FP8FG_GEMM_E8M0_SCALES if pow2 else B.FP8FG_GEMM_DEFAULT
+
+    def gemm():
+        B.fp8_gemm_blockscaled(M, N, K, st["qa"], K, st["sa"], 1, M, st["qb"], K, st["sb"], 1,
+                               N // 128, B.FP8FG_BSCALE_BLOCK128, st["c"], B.FP8FG_BF16, N, flags,
+                               stream)
+
+    for _ in range(args.warmup):
+        gemm()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        gemm()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"kernel": args.kernel, "ms": round(ms, 4),
+                      "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,6 +215,10 @@ def main():
             c=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     stream = torch.cuda.current_stream(dev)
     B = binding
+
+    if args.kernel:
+        kernel_only(args, M, N, K, sets[0], stream, B)
+        return
 
     def step(st, ev=None):
         if ev is not None:
