@@ -412,6 +412,35 @@ def test_e8m0_wide_tiles_grouped_ragged_and_empty_experts():
     e8m0_wide_check(qao, sao, None, None, "e8m0 wide grouped", offsets=off, qbs=qbs, sbs=sbs)
 
 
+@pytest.mark.parametrize("path", ["wide", "narrow", "n128", "e8m0", "e8m0_n128", "fp8_mfma",
+                                  "no_promotion", "col_scales", "grouped"])
+def test_empty_contraction_writes_zeros(path):
+    """K = 0 (no K groups): every kernel writes C = 0 over the whole output,
+    the empty sum of the oracle, and nothing past it."""
+    M = 200
+    N = 128 if path in ("n128", "e8m0_n128") else 256
+    dummy = torch.zeros(64, dtype=torch.uint8, device=DEV)          # operands: never read
+    one = torch.ones(1, dtype=torch.float32, device=DEV)            # scales, broadcast
+    cbuf = torch.full((M + 1, N), 7.0, dtype=torch.float32, device=DEV)
+    c = cbuf[:M]
+    flags = {"e8m0": B.FP8FG_GEMM_E8M0_SCALES, "e8m0_n128": B.FP8FG_GEMM_E8M0_SCALES,
+             "fp8_mfma": B.FP8FG_GEMM_FP8_MFMA, "no_promotion": B.FP8FG_GEMM_NO_PROMOTION}.get(path, 0)
+    mode = B.FP8FG_BSCALE_COL if path == "col_scales" else B.FP8FG_BSCALE_BLOCK128
+    with tiles(path if path in ("wide", "narrow") else None):
+        if path == "grouped":
+            offs = torch.tensor([0, 0, 150, 150, M], dtype=torch.int32, device=DEV)
+            B.fp8_grouped_gemm_blockscaled(4, offs, M, N, 0, dummy, 0, one, 0, 0, dummy, 0, 0, one, 0, 0,
+                                           0, c, B.FP8FG_F32, N, flags)
+        else:
+            B.fp8_gemm_blockscaled(M, N, 0, dummy, 0, one, 0, 0, dummy, 0, one, 0, 0, mode, c,
+                                   B.FP8FG_F32, N, flags)
+    h = host(cbuf)
+    ref = oracle.gemm_blockscaled(np.zeros((M, 0), np.uint8), np.zeros((M, 0)), np.zeros((0, N), np.uint8),
+                                  np.zeros((0, N // 128)))
+    assert np.array_equal(h[:M], ref) and np.all(h[:M] == 0.0)
+    assert np.all(h[M] == 7.0)
+
+
 # ---------------------------------------------------------------- grouped
 def grouped_case(counts, N, K, seed, what):
     counts = np.asarray(counts, np.int64)
