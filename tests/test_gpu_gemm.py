@@ -504,6 +504,16 @@ def test_streaming_kernel_bitwise_equals_tiled_kernel(N):
         assert torch.equal(big[7:47], grp)
 
 
+def test_grouped_256_experts():
+    # a DeepSeek-V3-sized expert count: 2048 tokens over 256 experts (a few
+    # rows each, many empty); both tile shapes, every expert's rows checked
+    rng = np.random.default_rng(57)
+    counts = rng.multinomial(2048, np.full(256, 1 / 256))
+    counts[rng.choice(256, 40, replace=False)] = 0
+    say("256 experts: %d empty, at most %d rows" % (int(np.sum(counts == 0)), int(counts.max())))
+    grouped_case(counts, N=256, K=256, seed=58, what="grouped G=256")
+
+
 def test_grouped_single_expert_equals_dense():
     qa, sa, offs, qb, sb, c32 = grouped_case([300], N=384, K=512, seed=40, what="grouped G=1")
     dense = host(T.gemm(qa, sa, qb[0], sb[0], out_dtype=torch.float32))
