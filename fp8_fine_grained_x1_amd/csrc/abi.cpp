@@ -184,7 +184,8 @@ int fp8_grouped_gemm_blockscaled(int64_t G, const int32_t* offsets, int64_t M_to
                                  void* stream) {
   if (G < 0 || M_total < 0 || b_gs < 0 || sb_gs < 0) return FP8FG_EINVAL;
   if (G == 0) return M_total == 0 ? FP8FG_OK : FP8FG_EINVAL;
-  if (G > 0x7FFFFFFF) return FP8FG_EUNSUPPORTED;
+  // the expert offsets are int32, so every row index must be one
+  if (G > 0x7FFFFFFF || M_total > 0x7FFFFFFF) return FP8FG_EUNSUPPORTED;
   const int rc = check_gemm_common(M_total, N, K, a, lda, sa, sa_ms, sa_ks, b, ldb, sb, sb_ns,
                                    sb_ks, FP8FG_BSCALE_BLOCK128, c, c_type, ldc, flags);
   if (rc != FP8FG_OK || M_total == 0 || N == 0) return rc;

@@ -107,6 +107,8 @@ enum {
  *   Alignment: x, q 16-byte aligned; ldx * sizeof(x_type) and ldq multiples
  *   of 16 bytes; s and x_scale 4-byte aligned.  rows == 0 or cols == 0 is a
  *   valid no-op.
+ *   Limits (FP8FG_EUNSUPPORTED beyond them): 1x128, at most 2^31 tiles
+ *   (rows * cols / 128); 128x1, rows / 128 <= 65535.
  */
 FP8FG_API int fp8_quantize_rowtile(const void* x, int x_type, int64_t rows, int64_t cols,
                          int64_t ldx, const float* x_scale, int64_t xs_rs,
@@ -125,6 +127,7 @@ FP8FG_API int fp8_quantize_rowtile(const void* x, int x_type, int64_t rows, int6
  *            rows contiguous -- the K-contiguous operand layout the GEMM
  *            reads when w is a K x N weight).
  *   Alignment as for fp8_quantize_rowtile.
+ *   Limit: rows / 128 <= 65535 (FP8FG_EUNSUPPORTED beyond).
  */
 FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_t cols,
                        int64_t ldw, int scale_rule, int transpose_out,
@@ -220,7 +223,9 @@ FP8FG_API int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_
  *   sb_e = sb + e * sb_gs (128x128 block scales, indexed as BLOCK128 above)
  *   Other arguments as for fp8_gemm_blockscaled (B scaling is BLOCK128).
  *   Requires G >= 1 (G == 0 with M_total == 0 is a no-op), K % 128 == 0,
- *   N % 128 == 0; b_gs a multiple of 16.
+ *   N % 128 == 0; b_gs a multiple of 16.  M_total and G at most 2^31 - 1
+ *   (the offsets are int32), plus the limits of fp8_gemm_blockscaled
+ *   (FP8FG_EUNSUPPORTED beyond them).
  */
 FP8FG_API int fp8_grouped_gemm_blockscaled(int64_t G, const int32_t* offsets,
                                  int64_t M_total, int64_t N, int64_t K,

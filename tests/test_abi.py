@@ -176,6 +176,53 @@ def test_grouped_validation(lib, kw, status):
     assert grouped(**kw) == status
 
 
+# Size limits: valid calls beyond what the kernels' 32-bit tile offsets,
+# grids or int32 expert offsets can address are refused with EUNSUPPORTED
+# (on the host, before any HIP call; every other argument is valid).
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=(1 << 30) + 1, cols=256, ldx=256, s_rs=2), B.FP8FG_EUNSUPPORTED),  # > 2^31 tiles
+    (dict(rows=1 << 30, cols=256, ldx=256, s_rs=2, x=None), B.FP8FG_EINVAL),      # checked first
+    (dict(tile=B.FP8FG_TILE_128x1, rows=128 * 65536, cols=128, ldx=128, ldq=128 * 65536),
+     B.FP8FG_EUNSUPPORTED),                                               # grid rows > 65535
+])
+def test_rowtile_size_limits(lib, kw, status):
+    assert rowtile(**kw) == status
+
+
+def test_block_size_limit(lib):
+    assert block(rows=128 * 65536, ldq=128 * 65536) == B.FP8FG_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lda=1 << 23),                                   # A row pitch: 256 rows * lda >= 2^31
+    dict(ldb=1 << 24),                                   # B row pitch: 256 rows * ldb >= 2^32
+    dict(K=1 << 31, lda=1 << 31, ldb=1 << 31),           # lda >= K: the pitch limit holds K
+    dict(sa_ms=1 << 21),                                 # A scale row stride
+    dict(sa_ks=(1 << 29) // 2),                          # sa_ks * K/128 >= 2^29 (K = 256)
+    dict(sb_ks=(1 << 29) // 2),
+    dict(b_scale_mode=B.FP8FG_BSCALE_COL, sb_ns=1 << 21),
+])
+def test_gemm_size_limits(lib, kw):
+    assert gemm(**kw) == B.FP8FG_EUNSUPPORTED
+
+
+def test_gemm_size_limits_are_exclusive(lib):
+    # one below each limit passes validation; with M = 0 nothing is launched
+    for kw in (dict(lda=(1 << 23) - 16), dict(ldb=(1 << 24) - 16), dict(sa_ms=(1 << 21) - 1),
+               dict(sa_ks=(1 << 29) // 2 - 1)):
+        assert gemm(M=0, **kw) == B.FP8FG_OK, kw
+        # and with rows, the limit check is not what rejects a bad pointer
+        assert gemm(a=None, **kw) == B.FP8FG_EINVAL, kw
+
+
+def test_grouped_size_limits(lib):
+    # int32 expert offsets cannot address more than 2^31 - 1 rows
+    assert grouped(M_total=1 << 31) == B.FP8FG_EUNSUPPORTED
+    assert grouped(M_total=1 << 31, offsets=None) == B.FP8FG_EUNSUPPORTED
+    assert grouped(G=1 << 31) == B.FP8FG_EUNSUPPORTED
+    assert grouped(lda=1 << 23) == B.FP8FG_EUNSUPPORTED
+
+
 def test_binding_raises_on_error(lib):
     with pytest.raises(B.Fp8fgError) as ei:
         B.fp8_quantize_rowtile(P16, 9, 1, 128, 128, None, 0, 0, 0, 0, P16, 128, P16, 1, 1, 0)
