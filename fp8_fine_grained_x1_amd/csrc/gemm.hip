@@ -132,6 +132,16 @@ struct KParams {
   int64_t n_base;  // first output column of this launch's tiles
 };
 
+// Compile-time flags for generic lambdas.
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Buffer resource over [base, base + bytes) (gfx9 raw buffer, stride 0).
@@ -563,20 +573,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
     wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
 
     // ---- epilogue: lane holds row lr of tile i, columns 8q + 4g .. +3 of tile j
-    const bool vec = p.vec_store != 0;
+    if constexpr (CT == 0) {
+      const bool vec = p.vec_store != 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wm * 64 + i * 32 + lr;
-      if (row >= rows_valid) continue;
-      const int64_t grow = row_base + row;
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + lr;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = n0 + wn * 64 + j * 32 + 8 * q + 4 * g;
-          const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n0 + wn * 64 + j * 32 + 8 * q + 4 * g;
+            const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+          }
+      }
+    } else {
+      // FP32 output: one copy of the stores per width, so that the aligned
+      // copy keeps its 16-byte stores (with a per-store choice the compiler
+      // merges the two forms into narrower ones).
+      auto epilogue = [&](auto vec_c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = wm * 64 + i * 32 + lr;
+          if (row >= rows_valid) continue;
+          const int64_t grow = row_base + row;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t col = n0 + wn * 64 + j * 32 + 8 * q + 4 * g;
+              const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              store_c4<CT>(p.c, grow * p.ldc + col, v, decltype(vec_c)::value);
+            }
         }
+      };
+      if (p.vec_store != 0)
+        epilogue(BoolTag<true>{});
+      else
+        epilogue(BoolTag<false>{});
     }
   } else {
     // ================================================================ FP8 MFMA
@@ -718,28 +754,62 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(KParams p
     wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
 
     // ---- epilogue: lane holds row fr of tile i, columns 4 (l/16) .. +3 of tile j
-    const bool vec = p.vec_store != 0;
+    if constexpr (CT == 0) {
+      const bool vec = p.vec_store != 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 64 + i * 16 + fr;
-      if (row >= rows_valid) continue;
-      const int64_t grow = row_base + row;
-      float rs = 1.0f;
-      if constexpr (!kPromote) rs = p.sa[grow * p.sa_ms];
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 64 + i * 16 + fr;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+        float rs = 1.0f;
+        if constexpr (!kPromote) rs = p.sa[grow * p.sa_ms];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
-        float v[4];
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][j][r];
-          if constexpr (!kPromote) {
-            const float cs = BMODE == 0 ? SB[(n0 >> 7) * p.sb_ns] : SB[(col + r) * p.sb_ns];
-            v[r] = v[r] * (rs * cs);
+          for (int r = 0; r < 4; ++r) {
+            v[r] = acc[i][j][r];
+            if constexpr (!kPromote) {
+              const float cs = BMODE == 0 ? SB[(n0 >> 7) * p.sb_ns] : SB[(col + r) * p.sb_ns];
+              v[r] = v[r] * (rs * cs);
+            }
+          }
+          store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+        }
+      }
+    } else {
+      // FP32 output: one copy of the stores per width, so that the aligned
+      // copy keeps its 16-byte stores (with a per-store choice the compiler
+      // merges the two forms into narrower ones).
+      auto epilogue = [&](auto vec_c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm * 64 + i * 16 + fr;
+          if (row >= rows_valid) continue;
+          const int64_t grow = row_base + row;
+          float rs = 1.0f;
+          if constexpr (!kPromote) rs = p.sa[grow * p.sa_ms];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = acc[i][j][r];
+              if constexpr (!kPromote) {
+                const float cs = BMODE == 0 ? SB[(n0 >> 7) * p.sb_ns] : SB[(col + r) * p.sb_ns];
+                v[r] = v[r] * (rs * cs);
+              }
+            }
+            store_c4<CT>(p.c, grow * p.ldc + col, v, decltype(vec_c)::value);
           }
         }
-        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
-      }
+      };
+      if (p.vec_store != 0)
+        epilogue(BoolTag<true>{});
+      else
+        epilogue(BoolTag<false>{});
     }
   }
 }
@@ -779,7 +849,8 @@ struct __align__(16) Stage2 {
   uint8_t b[64 * JT * kBK];
 };
 
-template <int CT, bool GROUPED, int JT>
+
+template <int CT, int JT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
   constexpr int kBNT = 64 * JT;         // workgroup tile columns
   constexpr int kWN = 32 * JT;          // wave tile columns
@@ -797,7 +868,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
   const int wn = wave & 1;   // columns wn*kWN .. +kWN
 
   // ---- tile decode
-  const int id = tile_id<GROUPED>(p, kBM);
+  const int id = tile_id<false>(p, kBM);
   if (id < 0) return;
   const uint8_t* A = p.a;
   const uint8_t* B = p.b;
@@ -805,30 +876,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
   int64_t row_base = 0;
   int rows_valid = 0;
   int tn = 0;
-  if constexpr (GROUPED) {
-    int t = id;
-    int e = 0;
-    bool found = false;
-    for (; e < p.G; ++e) {
-      const int64_t seg0 = p.offsets[e];
-      const int64_t seg1 = p.offsets[e + 1];
-      const int tm_e = (int)((seg1 - seg0 + kBM - 1) / kBM);
-      const int cnt = tm_e * p.tiles_n;
-      if (t < cnt) {
-        int tm;
-        grouped_order(t, tm_e, p.tiles_n, tm, tn);
-        row_base = seg0 + (int64_t)tm * kBM;
-        const int64_t rem = seg1 - row_base;
-        rows_valid = rem < kBM ? (int)rem : kBM;
-        found = true;
-        break;
-      }
-      t -= cnt;
-    }
-    if (!found) return;
-    B += (int64_t)e * p.b_gs;
-    SB += (int64_t)e * p.sb_gs;
-  } else {
+  {
     const int tiles_m = (int)((p.M + kBM - 1) / kBM);
     int tm;
     grouped_order(id, tiles_m, p.tiles_n, tm, tn);
@@ -1069,24 +1117,467 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
 
   // ---- epilogue: C = D * mc * 2^ec; lane holds row lr of row tile i,
   // columns 8q + 4g .. +3 of column tile j
-  const bool vec = p.vec_store != 0;
+  if constexpr (CT == 0) {
+    const bool vec = p.vec_store != 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = wm * 64 + i * 32 + lr;
-    if (row >= rows_valid) continue;
-    const int64_t grow = row_base + row;
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + lr;
+      if (row >= rows_valid) continue;
+      const int64_t grow = row_base + row;
 #pragma unroll
-    for (int j = 0; j < JT; ++j)
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + wn * kWN + j * 32 + 8 * q + 4 * g;
-        const int c = kPerJ ? j : 0;
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = n0 + wn * kWN + j * 32 + 8 * q + 4 * g;
+          const int c = kPerJ ? j : 0;
+          float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i][c], ec[i][c]);
-        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+          for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i][c], ec[i][c]);
+          store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+        }
+    }
+  } else {
+    // FP32 output: one copy of the stores per width, so that the aligned
+    // copy keeps its 16-byte stores (with a per-store choice the compiler
+    // merges the two forms into narrower ones).
+    auto epilogue = [&](auto vec_c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + lr;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n0 + wn * kWN + j * 32 + 8 * q + 4 * g;
+            const int c = kPerJ ? j : 0;
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i][c], ec[i][c]);
+            store_c4<CT>(p.c, grow * p.ldc + col, v, decltype(vec_c)::value);
+          }
       }
+    };
+    if (p.vec_store != 0)
+      epilogue(BoolTag<true>{});
+    else
+      epilogue(BoolTag<false>{});
   }
+}
+
+
+// Tile of a grouped launch of the rescaled-accumulation kernel.  Each
+// expert's rows are cut into 256-row tiles, except that a last tile of at
+// most 128 rows is a 128-row tile (half the work of a 256-row one).  The
+// 256-row tiles of all experts take workgroups 0 .. nbig - 1 (renumbered
+// over the XCDs as in tile_id); the 128-row tiles take the workgroups from
+// the next multiple of 8 on, so that every XCD runs its share of them after
+// its 256-row tiles.  The launch holds at least ceil(M / 256) + G row tiles
+// of workgroups plus 7; those without a tile return false.
+__device__ __forceinline__ bool grouped_rescale_tile(const KParams& p, int& expert, int64_t& row_base,
+                                                     int& rows_valid, int& tn, bool& half) {
+  int nbig = 0, nhalf = 0;
+  for (int e = 0; e < p.G; ++e) {
+    const int64_t rows = (int64_t)p.offsets[e + 1] - p.offsets[e];
+    const int64_t tail = rows % kBM;
+    nbig += (int)(rows / kBM) + (tail > kBM / 2 ? 1 : 0);
+    nhalf += tail > 0 && tail <= kBM / 2 ? 1 : 0;
+  }
+  nbig *= p.tiles_n;
+  nhalf *= p.tiles_n;
+  const int big_end = (nbig + 7) & ~7;
+  const int b = (int)blockIdx.x;
+  int t;
+  if (b < nbig) {
+    half = false;
+    t = xcd_remap(b, nbig);
+  } else if (b >= big_end && b - big_end < nhalf) {
+    half = true;
+    t = xcd_remap(b - big_end, nhalf);  // big_end % 8 == 0: same XCD as b
+  } else {
+    return false;
+  }
+  for (int e = 0; e < p.G; ++e) {
+    const int64_t seg0 = p.offsets[e];
+    const int64_t seg1 = p.offsets[e + 1];
+    const int64_t rows = seg1 - seg0;
+    const int64_t tail = rows % kBM;
+    if (!half) {
+      const int tm_e = (int)(rows / kBM) + (tail > kBM / 2 ? 1 : 0);
+      const int cnt = tm_e * p.tiles_n;
+      if (t < cnt) {
+        int tm;
+        grouped_order(t, tm_e, p.tiles_n, tm, tn);
+        row_base = seg0 + (int64_t)tm * kBM;
+        const int64_t rem = seg1 - row_base;
+        rows_valid = rem < kBM ? (int)rem : kBM;
+        expert = e;
+        return true;
+      }
+      t -= cnt;
+    } else if (tail > 0 && tail <= kBM / 2) {
+      if (t < p.tiles_n) {
+        tn = t;
+        row_base = seg1 - tail;
+        rows_valid = (int)tail;
+        expert = e;
+        return true;
+      }
+      t -= p.tiles_n;
+    }
+  }
+  return false;
+}
+
+// The grouped form of gemm_rescale_kernel: the same arithmetic per output
+// element, on 256-row tiles plus the 128-row tiles that end experts with at
+// most 128 rows left (RT row tiles of 32 per wave, chosen per workgroup).
+// It is a kernel of its own because the form with two tile heights in one
+// kernel runs 1-3% slower on dense shapes, where it is never needed.
+template <int CT, int JT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_rescale_grouped_kernel(KParams p) {
+  constexpr int kBNT = 64 * JT;         // workgroup tile columns
+  constexpr int kWN = 32 * JT;          // wave tile columns
+  constexpr bool kPerJ = JT != 4;
+  constexpr int kDmaB = kBNT / (8 * kWaves);
+  // Two stages, the A and B parts of each their own LDS object (the K loop
+  // is unrolled by two).
+  __shared__ __align__(16) uint8_t s0a[kBM * kBK];
+  __shared__ __align__(16) uint8_t s0b[kBNT * kBK];
+  __shared__ __align__(16) uint8_t s1a[kBM * kBK];
+  __shared__ __align__(16) uint8_t s1b[kBNT * kBK];
+  struct StageRef {
+    uint8_t* a;
+    uint8_t* b;
+  };
+  const StageRef stage0{s0a, s0b}, stage1{s1a, s1b};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave >> 1;  // row group of the wave
+  const int wn = wave & 1;   // columns wn*kWN .. +kWN
+
+  // ---- tile decode
+  const uint8_t* A = p.a;
+  const uint8_t* B = p.b;
+  const float* SB = p.sb;
+  int64_t row_base = 0;
+  int rows_valid = 0;
+  int tn = 0;
+  bool half = false;  // a 128-row tile
+  {
+    int e = 0;
+    if (!grouped_rescale_tile(p, e, row_base, rows_valid, tn, half)) return;
+    B += (int64_t)e * p.b_gs;
+    SB += (int64_t)e * p.sb_gs;
+  }
+  const int64_t n0 = p.n_base + (int64_t)tn * kBNT;
+  const int nkb = (int)(p.K / kBK);
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + row_base * p.lda, (uint32_t)(rows_valid * p.lda));
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + n0 * p.ldb, (uint32_t)(kBNT * p.ldb));
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(p.a, 0u);
+  uint32_t b_off[kDmaB];
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    b_off[i] = (uint32_t)(r * p.ldb + (((lane & 7) ^ swz(r)) << 4));
+  }
+  const int g = lane >> 5;
+  const int lr = lane & 31;
+  constexpr int NB = kPerJ ? JT : 1;  // B scales per group and wave
+  const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(p.sa + row_base * p.sa_ms, 0xFFFFFFFFu);
+  __amdgpu_buffer_rsrc_t sb_rsrc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    sb_rsrc[j] = make_rsrc(SB + ((n0 + wn * kWN + 32 * j) >> 7) * p.sb_ns, 0xFFFFFFFFu);
+
+  // The rest is written for RT row tiles of 32 per wave: RT = 2 on 256-row
+  // tiles (wave rows wm*64 .. +64), RT = 1 on 128-row tiles (wm*32 .. +32).
+  // Every 32x32 output tile sees the same operations in the same order
+  // either way.
+  auto body = [&](auto rt_c) {
+    constexpr int RT = decltype(rt_c)::value;
+    constexpr int kDmaA = 32 * RT * 4 / (8 * kWaves);
+    // ---- copy sources: instruction i of wave w fills LDS rows (8i + w) * 8 .. +8
+    uint32_t a_off[kDmaA];
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) {
+      const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+      const int ra = r < rows_valid ? r : rows_valid - 1;  // ragged M: repeat the last row
+      a_off[i] = (uint32_t)(ra * p.lda + (((lane & 7) ^ swz(r)) << 4));
+    }
+    // Every group issues the same copies (empty ones past the last group).
+    auto issue = [&](int kb, const StageRef& S) {
+      const bool live = kb < nkb;
+      const uint32_t koff = live ? (uint32_t)kb * kBK : 0u;
+      const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : null_rsrc;
+      const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : null_rsrc;
+#pragma unroll
+      for (int i = 0; i < kDmaA; ++i) dma16(ra, a_off[i], koff, S.a + (i * kWaves + wave) * 1024);
+#pragma unroll
+      for (int i = 0; i < kDmaB; ++i) dma16(rb, b_off[i], koff, S.b + (i * kWaves + wave) * 1024);
+    };
+
+    // ---- scale sources: this lane's output row in row tile i is
+    // wm*32*RT + i*32 + lane % 32; column tile j of the wave lies in B scale
+    // block (n0 + wn*kWN + 32 j) / 128
+    uint32_t sa_off[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = wm * 32 * RT + i * 32 + lr;
+      sa_off[i] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * p.sa_ms * 4);
+    }
+    struct ScaleRegs {
+      float sa[RT];
+      float sb[NB];
+    };
+    auto load_scales = [&](int kb, ScaleRegs& s) {
+      const bool live = kb < nkb;
+      const __amdgpu_buffer_rsrc_t ra = live ? sa_rsrc : null_rsrc;
+      const uint32_t ka = live ? (uint32_t)(kb * p.sa_ks * 4) : 0u;
+      const uint32_t kbo = live ? (uint32_t)(kb * p.sb_ks * 4) : 0u;
+#pragma unroll
+      for (int i = 0; i < RT; ++i) s.sa[i] = load_f32(ra, sa_off[i], ka);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) s.sb[j] = load_f32(live ? sb_rsrc[j] : null_rsrc, 0u, kbo);
+    };
+
+    // Wave tile 32*RT x kWN = RT x JT tiles of 32x32.  B is the first MFMA
+    // operand, so accumulator element r of lane l is row lr of row tile i
+    // and column 8 (r / 4) + 4 g + r % 4 of column tile j.
+    v16f D[RT][JT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < JT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) D[i][j][r] = 0.f;
+    // D of (row tile i, scale column c) is expressed in units of
+    // mc * 2^ec, split into a mantissa in [0.25, 1] and an exponent; mc = 0
+    // before anything was accumulated.  emax is the largest exponent of a
+    // scale product taken so far.  c = j when scales differ per column tile,
+    // else 0.
+    float mc[RT][NB], rs[RT][NB];
+    int ec[RT][NB], emax[RT][NB];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        mc[i][j] = 0.f;
+        rs[i][j] = 1.f;
+        ec[i][j] = 0;
+        emax[i][j] = -(1 << 20);
+      }
+
+    // Top of group kb: the copies issued in group kb - 1 (this group's data)
+    // are the newest memory operations, so wait for all; after the barrier
+    // every wave's copies have landed and every wave has finished reading the
+    // other stage.
+    auto wait_group = [&]() {
+      wait_vmcnt<0>();
+      block_barrier();
+    };
+
+    // Rescale factors of a group: rs = (mc / m) * 2^(ec - e) for the group's
+    // scale product m * 2^e; the mantissa quotient lies in (0.25, 4), so
+    // nothing overflows before the exponent is applied (the reciprocal is
+    // refined by one Newton step).  Computed at the end of the previous group,
+    // off the critical path.
+    auto factors = [&](const ScaleRegs& sr) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const float a = sr.sa[i];
+        const float ma = __builtin_amdgcn_frexp_mantf(a);
+        const int ea = __builtin_amdgcn_frexp_expf(a);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float b = sr.sb[j];
+          float m = ma * __builtin_amdgcn_frexp_mantf(b);
+          int e = ea + __builtin_amdgcn_frexp_expf(b);
+          // below the floor (or a zero scale): accumulate in the floor units
+          const bool low = a == 0.f || b == 0.f || e < emax[i][j] - kDropExp;
+          m = low ? 1.0f : m;
+          e = low ? emax[i][j] - kDropExp : e;
+          float r = __builtin_amdgcn_rcpf(m);
+          r = __builtin_fmaf(__builtin_fmaf(-m, r, 1.0f), r, r);
+          rs[i][j] = __builtin_amdgcn_ldexpf(mc[i][j] * r, ec[i][j] - e);
+          mc[i][j] = m;
+          ec[i][j] = e;
+          emax[i][j] = e > emax[i][j] ? e : emax[i][j];
+        }
+      }
+    };
+
+    auto cvt8 = [](uint32_t lo, uint32_t hi, float sc) {
+      union {
+        v2bf p[4];
+        v8bf v;
+      } u;
+      u.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, false);
+      u.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, sc, true);
+      u.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, false);
+      u.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, sc, true);
+      return u.v;
+    };
+
+    // MFMAs and conversions of one K step, for the schedule hints below
+    constexpr int kMfmaPerStep = RT * JT;
+    constexpr int kValuPerMfma = 4 * (RT + JT) / kMfmaPerStep;
+
+    // Group kb loads the scales of group kb + 2 into the register set that
+    // held group kb's (consumed at the end of group kb - 1), and at its end
+    // forms the factors of group kb + 1 from scales loaded a group earlier.
+    auto group = [&](int kb, const StageRef& S, const StageRef& Nx, ScaleRegs& lsr, const ScaleRegs& fsr) {
+      wait_group();
+      uint4 ra[4][RT], rb[4][JT];
+      auto read_chunk = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+          const int row = wm * 32 * RT + i * 32 + lr;
+          ra[c][i] = *reinterpret_cast<const uint4*>(S.a + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+          const int row = wn * kWN + j * 32 + lr;
+          rb[c][j] = *reinterpret_cast<const uint4*>(S.b + row * 128 + (((4 * g + c) ^ swz(row)) << 4));
+        }
+      };
+      v8bf af[2][RT], bfr[2][JT];  // [step parity][tile]
+      auto convert = [&](int st) {
+        const int c = st >> 1, h = st & 1, par = st & 1;
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+          af[par][i] = h ? cvt8(ra[c][i].z, ra[c][i].w, 1.0f) : cvt8(ra[c][i].x, ra[c][i].y, 1.0f);
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+          bfr[par][j] = h ? cvt8(rb[c][j].z, rb[c][j].w, 1.0f) : cvt8(rb[c][j].x, rb[c][j].y, 1.0f);
+      };
+      read_chunk(0);
+      read_chunk(1);
+      __builtin_amdgcn_sched_barrier(0);
+      // scales of group kb + 2 and copies of group kb + 1 (into the other stage)
+      load_scales(kb + 2, lsr);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kb + 1, Nx);
+      __builtin_amdgcn_sched_barrier(0);
+      // the rescale runs while the fragment reads are in flight
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) D[i][j][r] *= rs[i][kPerJ ? j : 0];
+      convert(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // the 8 K steps
+      auto steps = [&]() {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int par = st & 1;
+          // chunk c + 1 is read at step 2c, one step before its first conversion
+          if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) read_chunk((st >> 1) + 1);
+          if (st + 1 < 8) convert(st + 1);
+#pragma unroll
+          for (int j = 0; j < JT; ++j)
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+              D[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[par][j], af[par][i], D[i][j], 0, 0, 0);
+          if (!(st & 1) && st >= 2 && (st >> 1) + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, RT + JT, 0);
+#pragma unroll
+          for (int m = 0; m < kMfmaPerStep; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (st + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // Raised wave priority while the MFMA steps run: when the two waves of a
+      // SIMD are out of phase, the one in its MFMA steps issues first and the
+      // other's conversions and rescale fill in (about 1% on config 2).
+      __builtin_amdgcn_s_setprio(1);
+      steps();
+      __builtin_amdgcn_s_setprio(0);
+      // the next group's factors, while this group's last MFMAs run (none
+      // after the last group: the epilogue needs this group's units)
+      if (kb + 1 < nkb) factors(fsr);
+    };
+
+    // The kernel arguments that only the epilogue reads are made to arrive
+    // before the K loop.  Scalar and LDS loads share one counter and scalar
+    // loads complete out of order, so one still in flight at the loop entry
+    // would turn the first fragment wait of every group into a full drain.
+    asm volatile("" ::"s"(p.c), "s"(p.ldc), "s"(p.vec_store));
+    ScaleRegs sr0{}, sr1{};
+    load_scales(0, sr0);
+    load_scales(1, sr1);
+    issue(0, stage0);
+    factors(sr0);
+    int kb = 0;
+    for (; kb + 2 <= nkb; kb += 2) {
+      group(kb, stage0, stage1, sr0, sr1);
+      group(kb + 1, stage1, stage0, sr1, sr0);
+    }
+    if (kb < nkb) group(kb, stage0, stage1, sr0, sr1);
+    wait_vmcnt<0>();  // no LDS copy may land after the workgroup ends
+
+    // ---- epilogue: C = D * mc * 2^ec; lane holds row lr of row tile i,
+    // columns 8q + 4g .. +3 of column tile j
+    if constexpr (CT == 0) {
+      const bool vec = p.vec_store != 0;
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int row = wm * 32 * RT + i * 32 + lr;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n0 + wn * kWN + j * 32 + 8 * q + 4 * g;
+            const int c = kPerJ ? j : 0;
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i][c], ec[i][c]);
+            store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+          }
+      }
+    } else {
+      // FP32 output: one copy of the stores per width, so that the aligned
+      // copy keeps its 16-byte stores (with a per-store choice the compiler
+      // merges the two forms into narrower ones).
+      auto epilogue = [&](auto vec_c) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+          const int row = wm * 32 * RT + i * 32 + lr;
+          if (row >= rows_valid) continue;
+          const int64_t grow = row_base + row;
+#pragma unroll
+          for (int j = 0; j < JT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t col = n0 + wn * kWN + j * 32 + 8 * q + 4 * g;
+              const int c = kPerJ ? j : 0;
+              float v[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][j][4 * q + t] * mc[i][c], ec[i][c]);
+              store_c4<CT>(p.c, grow * p.ldc + col, v, decltype(vec_c)::value);
+            }
+        }
+      };
+      if (p.vec_store != 0)
+        epilogue(BoolTag<true>{});
+      else
+        epilogue(BoolTag<false>{});
+    }
+  };
+
+  if (__builtin_amdgcn_readfirstlane((int)half))
+    body(IntTag<1>{});
+  else
+    body(IntTag<2>{});
 }
 
 // ===========================================================================
@@ -1368,20 +1859,46 @@ __global__ __launch_bounds__(64 * SW, (stream_blocks_per_cu<SW, S, KG>())) void 
 
   // ---- epilogue: C = D * mc * 2^ec; lane holds row lr of row tile i,
   // columns 8q + 4g .. +3 of the wave's 32
-  const bool vec = p.vec_store != 0;
+  if constexpr (CT == 0) {
+    const bool vec = p.vec_store != 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = i * 32 + lr;
-    if (row >= rows_valid) continue;
-    const int64_t grow = row_base + row;
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 32 + lr;
+      if (row >= rows_valid) continue;
+      const int64_t grow = row_base + row;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t col = n0 + wave * 32 + 8 * q + 4 * g;
-      float v[4];
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + wave * 32 + 8 * q + 4 * g;
+        float v[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][4 * q + t] * mc[i], ec[i]);
-      store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][4 * q + t] * mc[i], ec[i]);
+        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+      }
     }
+  } else {
+    // FP32 output: one copy of the stores per width, so that the aligned
+    // copy keeps its 16-byte stores (with a per-store choice the compiler
+    // merges the two forms into narrower ones).
+    auto epilogue = [&](auto vec_c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = i * 32 + lr;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = n0 + wave * 32 + 8 * q + 4 * g;
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = __builtin_amdgcn_ldexpf(D[i][4 * q + t] * mc[i], ec[i]);
+          store_c4<CT>(p.c, grow * p.ldc + col, v, decltype(vec_c)::value);
+        }
+      }
+    };
+    if (p.vec_store != 0)
+      epilogue(BoolTag<true>{});
+    else
+      epilogue(BoolTag<false>{});
   }
 }
 
@@ -1648,22 +2165,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(KParams p) {
 
   // epilogue: lane holds row lr of row tile i, columns 8q + 4g .. +3 of
   // column tile j; D = acc * u
-  const bool vec = p.vec_store != 0;
+  if constexpr (CT == 0) {
+    const bool vec = p.vec_store != 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = wm * 64 + i * 32 + lr;
-    if (row >= rows_valid) continue;
-    const int64_t grow = row_base + row;
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + lr;
+      if (row >= rows_valid) continue;
+      const int64_t grow = row_base + row;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+          float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * u[i];
-        store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * u[i];
+          store_c4<CT>(p.c, grow * p.ldc + col, v, vec);
+        }
+    }
+  } else {
+    // FP32 output: one copy of the stores per width, so that the aligned
+    // copy keeps its 16-byte stores (with a per-store choice the compiler
+    // merges the two forms into narrower ones).
+    auto epilogue = [&](auto vec_c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + lr;
+        if (row >= rows_valid) continue;
+        const int64_t grow = row_base + row;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] * u[i];
+            store_c4<CT>(p.c, grow * p.ldc + col, v, decltype(vec_c)::value);
+          }
       }
+    };
+    if (p.vec_store != 0)
+      epilogue(BoolTag<true>{});
+    else
+      epilogue(BoolTag<false>{});
   }
 }
 
@@ -1675,7 +2220,10 @@ hipError_t launch_mx(const KParams& kp, hipStream_t st) {
 
 template <int CT, bool GROUPED, int JT>
 hipError_t launch_rescale(const KParams& kp, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_rescale_kernel<CT, GROUPED, JT>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
+  if constexpr (GROUPED)
+    hipLaunchKernelGGL((gemm_rescale_grouped_kernel<CT, JT>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
+  else
+    hipLaunchKernelGGL((gemm_rescale_kernel<CT, JT>), dim3(kp.nblocks), dim3(kThreads), 0, st, kp);
   return hipGetLastError();
 }
 
@@ -1806,15 +2354,18 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   // The default path with block scales runs the rescaled-accumulation
   // kernel on 256-column tiles and possibly a second launch of 192-column
   // tiles, the split that fills the CUs best (for a grouped GEMM tiles_m
-  // counts the row tiles of the worst case).  Both tile widths compute
-  // every output element with the same operations in the same order.
+  // counts the row tiles of the worst case, and 7 more workgroups let the
+  // kernel start its 128-row tiles at a multiple of 8).  Both tile widths
+  // compute every output element with the same operations in the same
+  // order.
   if (mode == kModeExact && g.b_scale_mode == 0) {
     const ColumnPlan plan = plan_columns(tiles_m, g.N, device_cu_count());
+    const int spare = grouped ? 7 : 0;
     if (plan.n256 + plan.n192 > 0) {
       hipError_t e = hipSuccess;
       if (plan.n256 > 0) {
         kp.tiles_n = (int)plan.n256;
-        kp.nblocks = (int)(tiles_m * plan.n256);
+        kp.nblocks = (int)(tiles_m * plan.n256) + spare;
         e = g.c_type == 0 ? (grouped ? launch_rescale<0, true, 4>(kp, st) : launch_rescale<0, false, 4>(kp, st))
                           : (grouped ? launch_rescale<1, true, 4>(kp, st) : launch_rescale<1, false, 4>(kp, st));
         if (e != hipSuccess) return e;
@@ -1822,7 +2373,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
       if (plan.n192 > 0) {
         kp.n_base = 256 * plan.n256;
         kp.tiles_n = (int)plan.n192;
-        kp.nblocks = (int)(tiles_m * plan.n192);
+        kp.nblocks = (int)(tiles_m * plan.n192) + spare;
         e = g.c_type == 0 ? (grouped ? launch_rescale<0, true, 3>(kp, st) : launch_rescale<0, false, 3>(kp, st))
                           : (grouped ? launch_rescale<1, true, 3>(kp, st) : launch_rescale<1, false, 3>(kp, st));
       }
