@@ -23,6 +23,8 @@
 //     and multiplied with v_mfma_f32_32x32x16_bf16) accumulated in units of
 //     the current K group's scale, the accumulator rescaled once per group;
 //     256 x 256 and 256 x 192 tiles (described before the kernel);
+//   * gemm_rescale_grouped_kernel -- the same for grouped launches, where
+//     an expert's last tile of at most 128 rows runs as a 128-row tile;
 //   * gemm_stream_kernel -- the same arithmetic for few rows per expert
 //     (MoE decode) or a dense M <= 64: 64 x 128 tiles, weight streaming;
 //   * gemm_mx_kernel -- the E8M0-scale flag with block scales and N a
