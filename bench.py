@@ -267,9 +267,15 @@ def main():
         B.fp8_quantize_rowtile(st0["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128,
                                B.FP8FG_SCALE_POW2, qp, K, sp, 1, M, stream)
 
-    def timed(fn, reps=20):
-        for _ in range(3):
-            fn()
+    def timed(fn, reps=20, warm_s=0.1):
+        # After the host-side setup of a workload the GPU has idled for
+        # seconds, and its clock needs tens of milliseconds of load to come
+        # back: run the call for warm_s of wall time before timing it.
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
         for i in range(reps):
             ev[2 * i].record(stream)
