@@ -1095,7 +1095,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
     };
     // Raised wave priority while the MFMA steps run: when the two waves of a
     // SIMD are out of phase, the one in its MFMA steps issues first and the
-    // other's conversions and rescale fill in (about 1% on config 2).
+    // other's conversions and rescale fill in (about 1% on the 4096 x 7168 x
+    // 7168 GEMM).
     __builtin_amdgcn_s_setprio(1);
     steps();
     __builtin_amdgcn_s_setprio(0);
@@ -1244,7 +1245,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_grouped_kernel(KPara
   constexpr bool kPerJ = JT != 4;
   constexpr int kDmaB = kBNT / (8 * kWaves);
   // Two stages, the A and B parts of each their own LDS object (the K loop
-  // is unrolled by two).
+  // is unrolled by two).  With one object per stage, the pointer chains of
+  // the B fragment reads grow past the depth at which the compiler keeps
+  // their LDS alias scopes, and every group then waits for the next group's
+  // copies before those reads.
   __shared__ __align__(16) uint8_t s0a[kBM * kBK];
   __shared__ __align__(16) uint8_t s0b[kBNT * kBK];
   __shared__ __align__(16) uint8_t s1a[kBM * kBK];
@@ -1498,7 +1502,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_grouped_kernel(KPara
       };
       // Raised wave priority while the MFMA steps run: when the two waves of a
       // SIMD are out of phase, the one in its MFMA steps issues first and the
-      // other's conversions and rescale fill in (about 1% on config 2).
+      // other's conversions and rescale fill in (about 1% on the 4096 x 7168 x
+      // 7168 GEMM).
       __builtin_amdgcn_s_setprio(1);
       steps();
       __builtin_amdgcn_s_setprio(0);
