@@ -202,6 +202,58 @@ def strided_output_case(qa, sa, qb, sb, a, b, M, N, choice):
     check_gemm(hb[1:M + 1, 32:32 + N], ref, "strided, %s tiles" % choice)
 
 
+def unaligned_out(run, M, N, dt):
+    """run(out) into an [M][N + 1] buffer (odd row pitch: the kernels' scalar
+    store path) and into a contiguous [M][N] one (vector stores): the same
+    values bit for bit, and the extra column untouched."""
+    buf = torch.full((M, N + 1), 7.0, dtype=dt, device=DEV)
+    run(buf[:, :N])
+    dense = torch.empty((M, N), dtype=dt, device=DEV)
+    run(dense)
+    hb = host(buf)
+    assert np.array_equal(hb[:, :N], host(dense))
+    assert np.array_equal(hb[:, N], host(torch.full((M,), 7.0, dtype=dt, device=DEV)))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_unaligned_output_rows_every_kernel(dt):
+    # every GEMM kernel picks its store width from the output's alignment
+    # once per tile; this drives the unaligned (scalar) stores of each one
+    M, N, K = 130, 256, 384
+    a = rand_bits(M, K, seed=91)
+    b = rand_bits(K, N, seed=92, std=0.02)
+    qa, sa = T.quantize_1x128(bf16_dev(a))
+    qb, sb = T.quantize_block(bf16_dev(b))
+    for choice in ("wide", "narrow"):
+        with tiles(choice):
+            unaligned_out(lambda o: T.gemm(qa, sa, qb, sb, out=o), M, N, dt)
+    pa, psa = T.quantize_1x128(bf16_dev(a), pow2=True)
+    pb, psb = T.quantize_block(bf16_dev(b), pow2=True)
+    unaligned_out(lambda o: T.gemm(pa, psa, pb, psb, out=o, e8m0_scales=True), M, N, dt)
+    unaligned_out(lambda o: T.gemm(qa, sa, qb, sb, out=o, fp8_mfma=True), M, N, dt)
+    # column scales (the wgrad layout)
+    x = rand_bits(K, M + 126, seed=93)
+    dy = rand_bits(K, N, seed=94)
+    qx, sx = T.quantize_128x1(bf16_dev(x))
+    qd, sd = T.quantize_128x1(bf16_dev(dy))
+    unaligned_out(lambda o: T.gemm(qx, sx, qd, sd, out=o, col_scales=True), M + 126, N, dt)
+    # grouped: 256-row tiles, 128-row expert tails and an empty expert
+    counts = np.array([300, 0, 129, 37])
+    offs = torch.from_numpy(workloads.moe_offsets(counts).astype(np.int32)).to(DEV)
+    G, Mg = len(counts), int(counts.sum())
+    ag = rand_bits(Mg, K, seed=95)
+    qg, sg = T.quantize_1x128(bf16_dev(ag), pow2=True)
+    qbg = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    sbg = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device=DEV)
+    for e in range(G):
+        q, s_ = T.quantize_block(bf16_dev(rand_bits(K, N, seed=96 + e, std=0.02)))
+        qbg[e].copy_(q)
+        sbg[e].copy_(s_)
+    for choice in ("wide", "narrow"):
+        with tiles(choice):
+            unaligned_out(lambda o: T.grouped_gemm(qg, sg, offs, qbg, sbg, out=o), Mg, N, dt)
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 128, 256), (384, 512, 640)])
 def test_column_scales(M, N, K):
     # Wgrad layout: both operands 128x1-quantized along K (the token axis)
