@@ -4,6 +4,13 @@
 
 Objects go to ``_build/`` at the repository root; the shared library is
 written next to this file.  Every call recompiles.
+
+``build_host_sanitized()`` compiles the same sources with AddressSanitizer
+and UndefinedBehaviorSanitizer on the host code only (argument validation,
+launch planning; the GPU code is built as usual) into ``_build/hostsan/``,
+for the CPU test that runs the C-ABI argument matrix under the sanitizers.
+The sanitizer runtime is not linked in: the process that loads the library
+preloads it (``asan_runtime()``).
 """
 
 import concurrent.futures
@@ -39,9 +46,20 @@ DEVICE = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# host-only sanitizers: each option applies to the host compilation alone
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address,undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-g",
+]
+HOSTSAN_BUILD = os.path.join(BUILD, "hostsan")
+HOSTSAN_LIB = os.path.join(HOSTSAN_BUILD, "libfp8fg_hostsan.so")
+
+
+def _compile(src, outdir=BUILD, extra=()):
+    obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + COMMON + DEVICE + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
@@ -63,6 +81,32 @@ def build(verbose=True):
     if verbose:
         print("built", LIB)
     return LIB
+
+
+def asan_runtime():
+    """The clang AddressSanitizer runtime (with its UBSan handlers) that a
+    process loading the host-sanitized library must preload."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib",
+                                         "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("clang AddressSanitizer runtime not found under the ROCm tree")
+    return hits[-1]
+
+
+def build_host_sanitized():
+    """Objects and library with the host code under ASan + UBSan; returns
+    (library path, object paths)."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError("hipcc not found at %s" % HIPCC)
+    os.makedirs(HOSTSAN_BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, HOSTSAN_BUILD, HOST_SANITIZE), SOURCES))
+    cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", "-o", HOSTSAN_LIB] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    return HOSTSAN_LIB, objs
 
 
 if __name__ == "__main__":

@@ -42,7 +42,9 @@ int elem_size(int t) { return t == FP8FG_F32 ? 4 : (t == FP8FG_BF16 ? 2 : 1); }
 
 int launched(hipError_t e) { return e == hipSuccess ? FP8FG_OK : FP8FG_ELAUNCH; }
 
+// grids of the 128x128-block quantizers: one 256-thread workgroup per block
 constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxGridX = 0xFFFFFFFFll / 256;
 
 }  // namespace
 
@@ -59,8 +61,14 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
                       int b_scale_mode, void* c, int c_type, int64_t ldc, int flags) {
   if (b_scale_mode != FP8FG_BSCALE_BLOCK128 && b_scale_mode != FP8FG_BSCALE_COL) return FP8FG_EINVAL;
   if (c_type != FP8FG_BF16 && c_type != FP8FG_F32) return FP8FG_EINVAL;
-  if (flags & ~(FP8FG_GEMM_NO_PROMOTION | FP8FG_GEMM_FP8_MFMA | FP8FG_GEMM_E8M0_SCALES)) return FP8FG_EINVAL;
+  constexpr int kFp8Flags = FP8FG_GEMM_NO_PROMOTION | FP8FG_GEMM_FP8_MFMA | FP8FG_GEMM_E8M0_SCALES;
+  constexpr int kTileFlags = FP8FG_GEMM_TILES_WIDE | FP8FG_GEMM_TILES_NARROW;
+  if (flags & ~(kFp8Flags | kTileFlags)) return FP8FG_EINVAL;
   if ((flags & FP8FG_GEMM_E8M0_SCALES) && (flags & FP8FG_GEMM_NO_PROMOTION)) return FP8FG_EINVAL;
+  // a tile choice exists only on the default path with block scales
+  if ((flags & kTileFlags) == kTileFlags) return FP8FG_EINVAL;
+  if ((flags & kTileFlags) && ((flags & kFp8Flags) || b_scale_mode != FP8FG_BSCALE_BLOCK128))
+    return FP8FG_EINVAL;
   if (M < 0 || N < 0 || K < 0 || lda < 0 || ldb < 0 || ldc < 0) return FP8FG_EINVAL;
   if (sa_ms < 0 || sa_ks < 0 || sb_ns < 0 || sb_ks < 0) return FP8FG_EINVAL;
   if ((flags & FP8FG_GEMM_NO_PROMOTION) && (sa_ks != 0 || sb_ks != 0)) return FP8FG_EINVAL;
@@ -84,7 +92,15 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
   return FP8FG_OK;
 }
 
-constexpr int64_t kMaxBlocks = 0x7FFFFFFF;
+// HIP takes at most 2^32 - 1 work-items along a grid dimension.
+constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
+
+// Every launch the plan makes fits the grid limit for its workgroup size.
+bool grid_fits(const fp8fg::GemmPlan& pl) {
+  for (const fp8fg::GemmLaunch& l : pl.launch)
+    if (l.nblocks > kMaxGridItems / pl.threads) return false;
+  return true;
+}
 
 }  // namespace
 
@@ -131,7 +147,7 @@ int fp8_quantize_rowtile(const void* x, int x_type, int64_t rows, int64_t cols, 
     fp8fg::RowtileArgs a{x, x_type, rows, cols, ldx, scale_rule, q, ldq, s, s_rs, s_ts};
     return launched(fp8fg::launch_quant_1x128(a, st));
   }
-  if (rows / 128 > kMaxGridY) return FP8FG_EUNSUPPORTED;
+  if (rows / 128 > kMaxGridY || cols / 128 > kMaxGridX) return FP8FG_EUNSUPPORTED;
   fp8fg::Tile128Args a{x,     x_type, rows, cols, ldx, x_scale, xs_rs, xs_ts, scale_rule,
                        /*per_column=*/true, /*transpose=*/true, q, ldq, s, s_rs, s_ts};
   return launched(fp8fg::launch_quant_tile128(a, st));
@@ -151,7 +167,7 @@ int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_t cols, in
   if (!aligned(w, 16) || (ldw * elem_size(w_type)) % 16 || !aligned(q, 16) || ldq % 16 ||
       !aligned(s, 4))
     return FP8FG_EALIGN;
-  if (rows / 128 > kMaxGridY) return FP8FG_EUNSUPPORTED;
+  if (rows / 128 > kMaxGridY || cols / 128 > kMaxGridX) return FP8FG_EUNSUPPORTED;
   fp8fg::Tile128Args a{w,       w_type, rows, cols,       ldw,
                        nullptr, 0,      0,    scale_rule, /*per_column=*/false,
                        transpose_out != 0, q, ldq, s, s_rs, s_cs};
@@ -167,13 +183,13 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
   const int rc = check_gemm_common(M, N, K, a, lda, sa, sa_ms, sa_ks, b, ldb, sb, sb_ns, sb_ks,
                                    b_scale_mode, c, c_type, ldc, flags);
   if (rc != FP8FG_OK || M == 0 || N == 0) return rc;
-  const int64_t tm = fp8fg::gemm_tile_m();
-  if (((M + tm - 1) / tm) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
   fp8fg::GemmArgs g{M,  N,  K,  a,      lda,    sa, sa_ms,
                     sa_ks, b, ldb, sb, sb_ns, sb_ks, b_scale_mode,
                     c,  c_type, ldc, flags,
                     0,  nullptr, 0,  0};
-  return launched(fp8fg::launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+  const fp8fg::GemmPlan plan = fp8fg::plan_gemm(g, fp8fg::device_cu_count());
+  if (!grid_fits(plan)) return FP8FG_EUNSUPPORTED;
+  return launched(fp8fg::launch_gemm(g, plan, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int fp8_grouped_gemm_blockscaled(int64_t G, const int32_t* offsets, int64_t M_total, int64_t N,
@@ -192,13 +208,13 @@ int fp8_grouped_gemm_blockscaled(int64_t G, const int32_t* offsets, int64_t M_to
   if (!offsets) return FP8FG_EINVAL;
   if (!aligned(offsets, 4)) return FP8FG_EALIGN;
   if (b_gs % 16) return FP8FG_EALIGN;
-  const int64_t tm = fp8fg::gemm_tile_m();
-  if (((M_total + tm - 1) / tm + G) * (N / 128) > kMaxBlocks) return FP8FG_EUNSUPPORTED;
   fp8fg::GemmArgs g{M_total, N,  K,  a,      lda,    sa, sa_ms,
                     sa_ks,   b,  ldb, sb, sb_ns, sb_ks, FP8FG_BSCALE_BLOCK128,
                     c,       c_type, ldc, flags,
                     G,       offsets, b_gs, sb_gs};
-  return launched(fp8fg::launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+  const fp8fg::GemmPlan plan = fp8fg::plan_gemm(g, fp8fg::device_cu_count());
+  if (!grid_fits(plan)) return FP8FG_EUNSUPPORTED;
+  return launched(fp8fg::launch_gemm(g, plan, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

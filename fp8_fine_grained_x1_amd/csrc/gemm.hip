@@ -70,8 +70,6 @@
 // empty experts need no host synchronization.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "device_common.h"
 #include "fp8fg.h"
@@ -2258,8 +2256,6 @@ hipError_t launch_mode(const KParams& kp, int mode, bool grouped, hipStream_t st
 
 }  // namespace
 
-int64_t gemm_tile_m() { return kBM; }
-
 ColumnPlan plan_columns(int64_t tiles_m, int64_t N, int cus) {
   // Column tiles of 256 and 192 with 256 n256 + 192 n192 = N; the split
   // with the fewest CU rounds (a 192-column tile costs 3/4 of a 256-column
@@ -2287,20 +2283,70 @@ ColumnPlan plan_columns(int64_t tiles_m, int64_t N, int cus) {
   return best;
 }
 
-// Override of the choice between the 64x128 and the 256-row tiles of the
-// exact path, read from the environment at each call (for tests and
-// tuning; every choice gives the same result): FP8FG_GEMM_TILES=wide or
-// =narrow, anything else (or unset) chooses from the shape.
-enum class TileChoice { kAuto, kWide, kNarrow };
-static TileChoice tile_choice() {
-  const char* v = getenv("FP8FG_GEMM_TILES");
-  if (v == nullptr) return TileChoice::kAuto;
-  if (strcmp(v, "wide") == 0) return TileChoice::kWide;
-  if (strcmp(v, "narrow") == 0) return TileChoice::kNarrow;
-  return TileChoice::kAuto;
+GemmPlan plan_gemm(const GemmArgs& g, int cus) {
+  GemmPlan pl{};
+  pl.kernel = GemmKernel::kNone;
+  pl.mode = (g.flags & FP8FG_GEMM_NO_PROMOTION)  ? kModeFp8NoPromo
+            : (g.flags & FP8FG_GEMM_E8M0_SCALES) ? kModeFp8Mx
+            : (g.flags & FP8FG_GEMM_FP8_MFMA)    ? kModeFp8
+                                                 : kModeExact;
+  const bool grouped = g.G > 0;
+  const int64_t tiles_m = grouped ? (g.M + kBM - 1) / kBM + g.G : (g.M + kBM - 1) / kBM;
+  if (g.M == 0 || g.N == 0 || tiles_m == 0) return pl;
+  const bool block = g.b_scale_mode == FP8FG_BSCALE_BLOCK128;
+  // E8M0 scales with block scales and N % 256 == 0: 256 x 256 tiles.
+  if (pl.mode == kModeFp8Mx && block && g.N % 256 == 0) {
+    pl.kernel = GemmKernel::kMx;
+    pl.threads = kThreads;
+    pl.launch[0] = GemmLaunch{g.N / 256, 0, tiles_m * (g.N / 256)};
+    return pl;
+  }
+  // Exact path with block scales: the weight-streaming kernel on 64x128
+  // tiles, two workgroups per CU, for few rows per expert, a dense M of at
+  // most one 64-row tile, or a dense grid of 256x256 tiles that would fill
+  // at most half of the CUs (small M x N with a long K: per CU the 64x128
+  // tiles deliver about half the rate of the 256x256 ones, so they win once
+  // they keep at least twice the CUs busy).  Both tile shapes give every
+  // output element bit for bit the same value; the flags
+  // FP8FG_GEMM_TILES_WIDE / _NARROW fix the choice.
+  const int64_t wide_tiles = tiles_m * ((g.N + 255) / 256);
+  const bool narrow = (g.flags & FP8FG_GEMM_TILES_NARROW) ? true
+                      : (g.flags & FP8FG_GEMM_TILES_WIDE) ? false
+                      : grouped ? g.M <= kStreamRowsPerExpert * g.G
+                                : (g.M <= kWBM || wide_tiles * 2 <= cus);
+  if (pl.mode == kModeExact && block && narrow) {
+    const int64_t tm = grouped ? (g.M + kWBM - 1) / kWBM + g.G : (g.M + kWBM - 1) / kWBM;
+    const int64_t tn = g.N / (32 * kStreamWaves);
+    pl.kernel = GemmKernel::kStream;
+    pl.threads = 64 * kStreamWaves;
+    pl.launch[0] = GemmLaunch{tn, 0, tm * tn};
+    return pl;
+  }
+  // The default path with block scales runs the rescaled-accumulation
+  // kernel on 256-column tiles and possibly a second launch of 192-column
+  // tiles, the split that fills the CUs best (for a grouped GEMM tiles_m
+  // counts the row tiles of the worst case, and 7 more workgroups let the
+  // kernel start its 128-row tiles at a multiple of 8).  Both tile widths
+  // compute every output element with the same operations in the same
+  // order.
+  if (pl.mode == kModeExact && block) {
+    const ColumnPlan cp = plan_columns(tiles_m, g.N, cus);
+    const int64_t spare = grouped ? 7 : 0;
+    if (cp.n256 + cp.n192 > 0) {
+      pl.kernel = GemmKernel::kRescale;
+      pl.threads = kThreads;
+      if (cp.n256 > 0) pl.launch[0] = GemmLaunch{cp.n256, 0, tiles_m * cp.n256 + spare};
+      if (cp.n192 > 0) pl.launch[1] = GemmLaunch{cp.n192, 256 * cp.n256, tiles_m * cp.n192 + spare};
+      return pl;
+    }
+  }
+  pl.kernel = GemmKernel::kBlockscaled;
+  pl.threads = kThreads;
+  pl.launch[0] = GemmLaunch{g.N / kBN, 0, tiles_m * (g.N / kBN)};
+  return pl;
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& pl, hipStream_t st) {
   KParams kp;
   kp.M = g.M;
   kp.N = g.N;
@@ -2321,82 +2367,47 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   kp.b_gs = g.b_gs;
   kp.sb_gs = g.sb_gs;
   kp.G = (int)g.G;
-  const int mode = (g.flags & FP8FG_GEMM_NO_PROMOTION)  ? kModeFp8NoPromo
-                   : (g.flags & FP8FG_GEMM_E8M0_SCALES) ? kModeFp8Mx
-                   : (g.flags & FP8FG_GEMM_FP8_MFMA)    ? kModeFp8
-                                                        : kModeExact;
   const int esize = g.c_type == 0 ? 2 : 4;
   kp.vec_store = (reinterpret_cast<uintptr_t>(g.c) % (4 * esize) == 0) && (g.ldc % 4 == 0);
-  kp.n_base = 0;
   const bool grouped = g.G > 0;
-  const int64_t tiles_m = grouped ? (g.M + kBM - 1) / kBM + g.G : (g.M + kBM - 1) / kBM;
-  if (tiles_m == 0) return hipSuccess;
-  // E8M0 scales with block scales and N % 256 == 0: 256 x 256 tiles.
-  if (mode == kModeFp8Mx && g.b_scale_mode == 0 && g.N % 256 == 0) {
-    kp.tiles_n = (int)(g.N / 256);
-    kp.nblocks = (int)(tiles_m * kp.tiles_n);
-    return g.c_type == 0 ? (grouped ? launch_mx<0, true>(kp, st) : launch_mx<0, false>(kp, st))
-                         : (grouped ? launch_mx<1, true>(kp, st) : launch_mx<1, false>(kp, st));
-  }
-  // Exact path with block scales: the weight-streaming kernel on 64x128
-  // tiles, two workgroups per CU, for few rows per expert, a dense M of at
-  // most one 64-row tile, or a dense grid of 256x256 tiles that would fill
-  // at most half of the CUs (small M x N with a long K: per CU the 64x128
-  // tiles deliver about half the rate of the 256x256 ones, so they win once
-  // they keep at least twice the CUs busy).  Both tile shapes give every
-  // output element bit for bit the same value.
-  const TileChoice tc = tile_choice();
-  const int64_t wide_tiles = tiles_m * ((g.N + 255) / 256);
-  const bool narrow = tc == TileChoice::kNarrow ? true
-                      : tc == TileChoice::kWide ? false
-                      : grouped                  ? g.M <= kStreamRowsPerExpert * g.G
-                                                 : (g.M <= kWBM || wide_tiles * 2 <= device_cu_count());
-  if (mode == kModeExact && g.b_scale_mode == 0 && narrow) {
-    const int64_t tm = grouped ? (g.M + kWBM - 1) / kWBM + g.G : (g.M + kWBM - 1) / kWBM;
-    kp.tiles_n = (int)(g.N / (32 * kStreamWaves));
-    kp.nblocks = (int)(tm * kp.tiles_n);
-    return g.c_type == 0 ? (grouped ? launch_stream<0, true>(kp, st) : launch_stream<0, false>(kp, st))
-                         : (grouped ? launch_stream<1, true>(kp, st) : launch_stream<1, false>(kp, st));
-  }
-  // The default path with block scales runs the rescaled-accumulation
-  // kernel on 256-column tiles and possibly a second launch of 192-column
-  // tiles, the split that fills the CUs best (for a grouped GEMM tiles_m
-  // counts the row tiles of the worst case, and 7 more workgroups let the
-  // kernel start its 128-row tiles at a multiple of 8).  Both tile widths
-  // compute every output element with the same operations in the same
-  // order.
-  if (mode == kModeExact && g.b_scale_mode == 0) {
-    const ColumnPlan plan = plan_columns(tiles_m, g.N, device_cu_count());
-    const int spare = grouped ? 7 : 0;
-    if (plan.n256 + plan.n192 > 0) {
-      hipError_t e = hipSuccess;
-      if (plan.n256 > 0) {
-        kp.tiles_n = (int)plan.n256;
-        kp.nblocks = (int)(tiles_m * plan.n256) + spare;
-        e = g.c_type == 0 ? (grouped ? launch_rescale<0, true, 4>(kp, st) : launch_rescale<0, false, 4>(kp, st))
-                          : (grouped ? launch_rescale<1, true, 4>(kp, st) : launch_rescale<1, false, 4>(kp, st));
-        if (e != hipSuccess) return e;
-      }
-      if (plan.n192 > 0) {
-        kp.n_base = 256 * plan.n256;
-        kp.tiles_n = (int)plan.n192;
-        kp.nblocks = (int)(tiles_m * plan.n192) + spare;
-        e = g.c_type == 0 ? (grouped ? launch_rescale<0, true, 3>(kp, st) : launch_rescale<0, false, 3>(kp, st))
-                          : (grouped ? launch_rescale<1, true, 3>(kp, st) : launch_rescale<1, false, 3>(kp, st));
-      }
-      return e;
+  const bool bf = g.c_type == 0;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < 2 && e == hipSuccess; ++l) {
+    const GemmLaunch& L = pl.launch[l];
+    if (L.nblocks <= 0) continue;
+    kp.tiles_n = (int)L.tiles_n;
+    kp.n_base = L.n_base;
+    kp.nblocks = (int)L.nblocks;
+    switch (pl.kernel) {
+      case GemmKernel::kMx:
+        e = bf ? (grouped ? launch_mx<0, true>(kp, st) : launch_mx<0, false>(kp, st))
+               : (grouped ? launch_mx<1, true>(kp, st) : launch_mx<1, false>(kp, st));
+        break;
+      case GemmKernel::kStream:
+        e = bf ? (grouped ? launch_stream<0, true>(kp, st) : launch_stream<0, false>(kp, st))
+               : (grouped ? launch_stream<1, true>(kp, st) : launch_stream<1, false>(kp, st));
+        break;
+      case GemmKernel::kRescale:
+        if (l == 0)
+          e = bf ? (grouped ? launch_rescale<0, true, 4>(kp, st) : launch_rescale<0, false, 4>(kp, st))
+                 : (grouped ? launch_rescale<1, true, 4>(kp, st) : launch_rescale<1, false, 4>(kp, st));
+        else
+          e = bf ? (grouped ? launch_rescale<0, true, 3>(kp, st) : launch_rescale<0, false, 3>(kp, st))
+                 : (grouped ? launch_rescale<1, true, 3>(kp, st) : launch_rescale<1, false, 3>(kp, st));
+        break;
+      case GemmKernel::kBlockscaled:
+        if (bf)
+          e = g.b_scale_mode == 0 ? launch_mode<0, 0>(kp, pl.mode, grouped, st)
+                                  : launch_mode<0, 1>(kp, pl.mode, grouped, st);
+        else
+          e = g.b_scale_mode == 0 ? launch_mode<1, 0>(kp, pl.mode, grouped, st)
+                                  : launch_mode<1, 1>(kp, pl.mode, grouped, st);
+        break;
+      case GemmKernel::kNone:
+        break;
     }
   }
-  kp.tiles_n = (int)(g.N / kBN);
-  const int64_t nblocks = tiles_m * kp.tiles_n;
-  if (nblocks == 0) return hipSuccess;
-  kp.nblocks = (int)nblocks;
-  if (g.c_type == 0) {
-    return g.b_scale_mode == 0 ? launch_mode<0, 0>(kp, mode, grouped, st)
-                               : launch_mode<0, 1>(kp, mode, grouped, st);
-  }
-  return g.b_scale_mode == 0 ? launch_mode<1, 0>(kp, mode, grouped, st)
-                             : launch_mode<1, 1>(kp, mode, grouped, st);
+  return e;
 }
 
 }  // namespace fp8fg

@@ -60,9 +60,24 @@ struct GemmArgs {
   const int32_t* offsets;
   int64_t b_gs, sb_gs;
 };
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
-// Rows of A per workgroup tile of the GEMM kernels.
-int64_t gemm_tile_m();
+// Which GEMM kernel runs, and its launches (at most two: the default path's
+// 256- and 192-column tiles).  Computed on the host from the arguments alone
+// (and the CU count), before anything is enqueued, so that the caller can
+// check the grid sizes of exactly the launches that will be made.
+enum class GemmKernel { kNone, kMx, kStream, kRescale, kBlockscaled };
+struct GemmLaunch {
+  int64_t tiles_n;   // column tiles of this launch
+  int64_t n_base;    // first output column of this launch's tiles
+  int64_t nblocks;   // workgroups (0: no launch)
+};
+struct GemmPlan {
+  GemmKernel kernel;
+  int mode;          // arithmetic of gemm_blockscaled_kernel (exact / FP8 flags)
+  int threads;       // per workgroup
+  GemmLaunch launch[2];
+};
+GemmPlan plan_gemm(const GemmArgs& g, int cus);
+hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& plan, hipStream_t st);
 // Split of N into column tiles of 256 and 192 for the default GEMM path
 // (both zero: the path does not apply).  cus = 0 asks for 256-column tiles
 // only (grouped GEMM).

@@ -79,7 +79,14 @@ enum {
      as its E8M0 operand scales (the microscaling form; implies
      FP8FG_GEMM_FP8_MFMA and its precision; fastest with power-of-two
      scales) */
-  FP8FG_GEMM_E8M0_SCALES = 4
+  FP8FG_GEMM_E8M0_SCALES = 4,
+  /* default path with BLOCK128 scales only: fix the tile shape instead of
+     choosing it from the sizes -- WIDE the 256-row tiles, NARROW the 64x128
+     weight-streaming tiles.  Every choice gives the same result bit for bit
+     (for N >= 256); for tests and tuning.  Setting both, or either together
+     with an FP8 flag or COL scales, is FP8FG_EINVAL. */
+  FP8FG_GEMM_TILES_WIDE = 8,
+  FP8FG_GEMM_TILES_NARROW = 16
 };
 
 /*
@@ -108,7 +115,8 @@ enum {
  *   of 16 bytes; s and x_scale 4-byte aligned.  rows == 0 or cols == 0 is a
  *   valid no-op.
  *   Limits (FP8FG_EUNSUPPORTED beyond them): 1x128, at most 2^31 tiles
- *   (rows * cols / 128); 128x1, rows / 128 <= 65535.
+ *   (rows * cols / 128); 128x1, rows / 128 <= 65535 and
+ *   cols / 128 <= (2^32 - 1) / 256.
  */
 FP8FG_API int fp8_quantize_rowtile(const void* x, int x_type, int64_t rows, int64_t cols,
                          int64_t ldx, const float* x_scale, int64_t xs_rs,
@@ -127,7 +135,8 @@ FP8FG_API int fp8_quantize_rowtile(const void* x, int x_type, int64_t rows, int6
  *            rows contiguous -- the K-contiguous operand layout the GEMM
  *            reads when w is a K x N weight).
  *   Alignment as for fp8_quantize_rowtile.
- *   Limit: rows / 128 <= 65535 (FP8FG_EUNSUPPORTED beyond).
+ *   Limits: rows / 128 <= 65535, cols / 128 <= (2^32 - 1) / 256
+ *   (FP8FG_EUNSUPPORTED beyond).
  */
 FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_t cols,
                        int64_t ldw, int scale_rule, int transpose_out,
@@ -157,10 +166,9 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *   counts); N = 128 and per-column scales use a kernel that promotes
  *   separate group sums, whose rounding differs within the same accuracy.
  *   Small grids (few 256x256 tiles for the compute units, as with a small
- *   M x N and a long K) run on 64x128 tiles.  The environment variable
- *   FP8FG_GEMM_TILES=wide or =narrow, read at each call, fixes the choice
- *   between the 256-row and the 64x128 tiles of this path (for tests and
- *   tuning).
+ *   M x N and a long K) run on 64x128 tiles; the flags
+ *   FP8FG_GEMM_TILES_WIDE / FP8FG_GEMM_TILES_NARROW fix that choice.  The
+ *   library reads no environment variables.
  *
  *   a : E4M3 [M][K] (K contiguous), sa(m, kb) = sa[m * sa_ms + kb * sa_ks].
  *   b : E4M3 [N][K] (K contiguous -- the transposed weight),
@@ -170,8 +178,9 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *       or F32, row pitch ldc.
  *   Requires K % 128 == 0 and N % 128 == 0; any M >= 0.  Scale strides may
  *   be 0 (broadcast).
- *   flags: a bit set of FP8FG_GEMM_NO_PROMOTION, FP8FG_GEMM_FP8_MFMA and
- *       FP8FG_GEMM_E8M0_SCALES.
+ *   flags: a bit set of FP8FG_GEMM_NO_PROMOTION, FP8FG_GEMM_FP8_MFMA,
+ *       FP8FG_GEMM_E8M0_SCALES and one of FP8FG_GEMM_TILES_WIDE /
+ *       FP8FG_GEMM_TILES_NARROW.
  *       NO_PROMOTION: the whole K is summed in the FP8 matrix-core
  *       accumulator and scaled once by sa(m, 0) * sb(0, n); only meaningful
  *       for per-tensor scales, so sa_ks and sb_ks must then be 0.
@@ -200,7 +209,9 @@ FP8FG_API int fp8_quantize_block(const void* w, int w_type, int64_t rows, int64_
  *   Limits (FP8FG_EUNSUPPORTED beyond them; the kernels address a tile with
  *   32-bit offsets): lda < 2^23, ldb < 2^24, K < 2^31; when promoting,
  *   sa_ms < 2^21 (and sb_ns < 2^21 in the COL mode) and
- *   sa_ks * K/128, sb_ks * K/128 < 2^29.
+ *   sa_ks * K/128, sb_ks * K/128 < 2^29; every launch of the chosen kernel
+ *   within HIP's 2^32 - 1 work-items per grid dimension (the workgroup
+ *   count is computed for the tile shape that will run).
  */
 FP8FG_API int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                          int64_t lda, const float* sa, int64_t sa_ms,

@@ -1,7 +1,6 @@
 """Shared plumbing for the GPU parity tests: moving seeded inputs to the
 device, caching the large workloads, and the GEMM tolerance check."""
 
-import contextlib
 import functools
 import os
 import sys
@@ -18,25 +17,6 @@ DEV = "cuda:0"
 # over entries with |ref| > 1e-2 * rms(ref)).
 TOL_FROB = 1e-5
 TOL_MAXREL = 1e-3
-
-
-@contextlib.contextmanager
-def tiles(choice):
-    """The exact GEMM path's tile choice for the calls inside: 'wide'
-    (256-row tiles), 'narrow' (64x128 tiles) or None (chosen from the shape).
-    Every choice gives the same result bit for bit."""
-    old = os.environ.get("FP8FG_GEMM_TILES")
-    if choice is None:
-        os.environ.pop("FP8FG_GEMM_TILES", None)
-    else:
-        os.environ["FP8FG_GEMM_TILES"] = choice
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("FP8FG_GEMM_TILES", None)
-        else:
-            os.environ["FP8FG_GEMM_TILES"] = old
 
 
 def say(msg):

@@ -136,7 +136,13 @@ def test_block_validation(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(b_scale_mode=3), B.FP8FG_EINVAL),
     (dict(c_type=B.FP8FG_E4M3), B.FP8FG_EINVAL),
-    (dict(flags=8), B.FP8FG_EINVAL),
+    (dict(flags=32), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_TILES_WIDE | B.FP8FG_GEMM_TILES_NARROW), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_TILES_WIDE | B.FP8FG_GEMM_FP8_MFMA), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_TILES_NARROW | B.FP8FG_GEMM_E8M0_SCALES), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_TILES_NARROW, b_scale_mode=B.FP8FG_BSCALE_COL), B.FP8FG_EINVAL),
+    (dict(flags=B.FP8FG_GEMM_TILES_WIDE, c=None), B.FP8FG_EINVAL),   # flag accepted, then null c
+    (dict(flags=B.FP8FG_GEMM_TILES_NARROW, c=None), B.FP8FG_EINVAL),
     (dict(flags=B.FP8FG_GEMM_FP8_MFMA, c=None), B.FP8FG_EINVAL),   # flag accepted, then null c
     (dict(flags=B.FP8FG_GEMM_E8M0_SCALES, c=None), B.FP8FG_EINVAL),
     (dict(flags=B.FP8FG_GEMM_E8M0_SCALES | B.FP8FG_GEMM_FP8_MFMA, c=None), B.FP8FG_EINVAL),
@@ -191,6 +197,10 @@ def test_rowtile_size_limits(lib, kw, status):
 
 def test_block_size_limit(lib):
     assert block(rows=128 * 65536, ldq=128 * 65536) == B.FP8FG_EUNSUPPORTED
+    # grid columns: at most (2^32 - 1) / 256 workgroups of 256 threads
+    assert block(rows=128, cols=1 << 31, ldw=1 << 31, ldq=128) == B.FP8FG_EUNSUPPORTED
+    assert rowtile(tile=B.FP8FG_TILE_128x1, rows=128, cols=1 << 31, ldx=1 << 31, ldq=128,
+                   s_rs=1) == B.FP8FG_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("kw", [
@@ -213,6 +223,16 @@ def test_gemm_size_limits_are_exclusive(lib):
         assert gemm(M=0, **kw) == B.FP8FG_OK, kw
         # and with rows, the limit check is not what rejects a bad pointer
         assert gemm(a=None, **kw) == B.FP8FG_EINVAL, kw
+
+
+def test_gemm_grid_limit_counts_the_tiles_that_launch(lib):
+    # 2^30 rows on the 64x128 tiles: 2^24 workgroups of 256 threads, one past
+    # HIP's 2^32 - 1 work-items (on the 256-row tiles the same call needs a
+    # quarter of that); 2^31 rows on the 256x256 tiles: 2^23 workgroups of 512
+    big = dict(K=128, lda=128, ldb=128, sa_ms=1, sa_ks=1)
+    assert gemm(M=1 << 30, flags=B.FP8FG_GEMM_TILES_NARROW, **big) == B.FP8FG_EUNSUPPORTED
+    assert gemm(M=1 << 31, N=256, ldc=256, flags=B.FP8FG_GEMM_TILES_WIDE, **big) == B.FP8FG_EUNSUPPORTED
+    assert grouped(G=1, M_total=(1 << 30), flags=B.FP8FG_GEMM_TILES_NARROW, **big) == B.FP8FG_EUNSUPPORTED
 
 
 def test_grouped_size_limits(lib):

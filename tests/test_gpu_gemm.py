@@ -17,7 +17,7 @@ from fp8_fine_grained_x1_amd import binding as B
 from fp8_fine_grained_x1_amd import tensors as T
 from fp8_fine_grained_x1_amd import workloads
 from gpu_util import (DEV, bf16_dev, check_bf16_output, check_gemm, f32, f32_dev, fp8_mfma_bound,
-                      host, say, tiles, workload)
+                      host, say, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,9 +49,8 @@ def dense_case(a_bits, b_bits, a_pow2=False, b_pow2=False, what="", scale_layout
     # the 256-row choice promotes separate group sums)
     outs = {}
     for choice in ("wide", "narrow", None):
-        with tiles(choice):
-            h32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
-            h16 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16))
+        h32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, tiles=choice))
+        h16 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16, tiles=choice))
         check_gemm(h32, ref, "%s (%s tiles)" % (what, choice or "chosen"))
         check_bf16_output(h16, h32, ref)
         outs[choice] = (h32, h16)
@@ -95,8 +94,7 @@ def test_identity_weights_bit_exact():
     qao, sao = oracle.quantize_1x128(f32(a))
     expect = (oracle.decode(qao).astype(np.float32) * np.repeat(sao, 128, axis=1)).astype(np.float32)
     for choice in ("wide", "narrow"):
-        with tiles(choice):
-            c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+        c32 = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, tiles=choice))
         assert np.array_equal(c32, expect), choice
 
 
@@ -143,8 +141,7 @@ def test_extreme_group_scales_per_row(N):
     qao, sao = oracle.quantize_1x128(x)
     qbo, sbo = oracle.quantize_128x128(w)
     assert np.array_equal(host(qa), qao) and np.array_equal(host(sa), sao)
-    with tiles("wide"):
-        c = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+    c = host(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, tiles="wide"))
     _check_rows(c, oracle.gemm_blockscaled(qao, sao, qbo, sbo))
 
 
@@ -186,14 +183,13 @@ def test_strided_output_and_guard_bands():
     qa, sa = T.quantize_1x128(bf16_dev(a))
     qb, sb = T.quantize_block(bf16_dev(b))
     for choice in ("wide", "narrow"):
-        with tiles(choice):
-            strided_output_case(qa, sa, qb, sb, a, b, M, N, choice)
+        strided_output_case(qa, sa, qb, sb, a, b, M, N, choice)
 
 
 def strided_output_case(qa, sa, qb, sb, a, b, M, N, choice):
     cbuf = torch.full((M + 2, N + 64), 12345.0, dtype=torch.float32, device=DEV)
     c = cbuf[1:M + 1, 32:32 + N]
-    T.gemm(qa, sa, qb, sb, out=c)
+    T.gemm(qa, sa, qb, sb, out=c, tiles=choice)
     hb = host(cbuf)
     mask = np.ones_like(hb, dtype=bool)
     mask[1:M + 1, 32:32 + N] = False
@@ -225,8 +221,7 @@ def test_unaligned_output_rows_every_kernel(dt):
     qa, sa = T.quantize_1x128(bf16_dev(a))
     qb, sb = T.quantize_block(bf16_dev(b))
     for choice in ("wide", "narrow"):
-        with tiles(choice):
-            unaligned_out(lambda o: T.gemm(qa, sa, qb, sb, out=o), M, N, dt)
+        unaligned_out(lambda o: T.gemm(qa, sa, qb, sb, out=o, tiles=choice), M, N, dt)
     pa, psa = T.quantize_1x128(bf16_dev(a), pow2=True)
     pb, psb = T.quantize_block(bf16_dev(b), pow2=True)
     unaligned_out(lambda o: T.gemm(pa, psa, pb, psb, out=o, e8m0_scales=True), M, N, dt)
@@ -250,8 +245,7 @@ def test_unaligned_output_rows_every_kernel(dt):
         qbg[e].copy_(q)
         sbg[e].copy_(s_)
     for choice in ("wide", "narrow"):
-        with tiles(choice):
-            unaligned_out(lambda o: T.grouped_gemm(qg, sg, offs, qbg, sbg, out=o), Mg, N, dt)
+        unaligned_out(lambda o: T.grouped_gemm(qg, sg, offs, qbg, sbg, out=o, tiles=choice), Mg, N, dt)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 256), (384, 512, 640)])
@@ -478,14 +472,14 @@ def test_empty_contraction_writes_zeros(path):
     flags = {"e8m0": B.FP8FG_GEMM_E8M0_SCALES, "e8m0_n128": B.FP8FG_GEMM_E8M0_SCALES,
              "fp8_mfma": B.FP8FG_GEMM_FP8_MFMA, "no_promotion": B.FP8FG_GEMM_NO_PROMOTION}.get(path, 0)
     mode = B.FP8FG_BSCALE_COL if path == "col_scales" else B.FP8FG_BSCALE_BLOCK128
-    with tiles(path if path in ("wide", "narrow") else None):
-        if path == "grouped":
-            offs = torch.tensor([0, 0, 150, 150, M], dtype=torch.int32, device=DEV)
-            B.fp8_grouped_gemm_blockscaled(4, offs, M, N, 0, dummy, 0, one, 0, 0, dummy, 0, 0, one, 0, 0,
-                                           0, c, B.FP8FG_F32, N, flags)
-        else:
-            B.fp8_gemm_blockscaled(M, N, 0, dummy, 0, one, 0, 0, dummy, 0, one, 0, 0, mode, c,
-                                   B.FP8FG_F32, N, flags)
+    flags |= T.tile_flags(path if path in ("wide", "narrow") else None)
+    if path == "grouped":
+        offs = torch.tensor([0, 0, 150, 150, M], dtype=torch.int32, device=DEV)
+        B.fp8_grouped_gemm_blockscaled(4, offs, M, N, 0, dummy, 0, one, 0, 0, dummy, 0, 0, one, 0, 0,
+                                       0, c, B.FP8FG_F32, N, flags)
+    else:
+        B.fp8_gemm_blockscaled(M, N, 0, dummy, 0, one, 0, 0, dummy, 0, one, 0, 0, mode, c,
+                               B.FP8FG_F32, N, flags)
     h = host(cbuf)
     ref = oracle.gemm_blockscaled(np.zeros((M, 0), np.uint8), np.zeros((M, 0)), np.zeros((0, N), np.uint8),
                                   np.zeros((0, N // 128)))
@@ -518,9 +512,8 @@ def grouped_case(counts, N, K, seed, what):
     if N >= 256:
         # both tile shapes of the exact path give the same bits
         for choice in ("wide", "narrow"):
-            with tiles(choice):
-                assert np.array_equal(host(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32)),
-                                      c32), choice
+            assert np.array_equal(host(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32,
+                                                      tiles=choice)), c32), choice
     return qa, sa, offs, qb, sb, c32
 
 
@@ -547,8 +540,7 @@ def test_streaming_kernel_bitwise_equals_tiled_kernel(N):
     qa, sa = T.quantize_1x128(bf16_dev(a))
     qb, sb = T.quantize_block(bf16_dev(b))
     for dt in (torch.float32, torch.bfloat16):
-        with tiles("wide"):
-            big = T.gemm(qa, sa, qb, sb, out_dtype=dt)
+        big = T.gemm(qa, sa, qb, sb, out_dtype=dt, tiles="wide")
         small = T.gemm(qa[100:164], sa[100:164], qb, sb, out_dtype=dt)
         assert torch.equal(big[100:164], small)
         offs = torch.tensor([0, 40], dtype=torch.int32, device=DEV)
@@ -606,8 +598,7 @@ def dense_full_size(w, pow2_a=False):
     c16 = T.gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16)
     # ... equal, over the whole output, those of both forced choices
     for choice in ("wide", "narrow"):
-        with tiles(choice):
-            assert torch.equal(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32), c32), choice
+        assert torch.equal(T.gemm(qa, sa, qb, sb, out_dtype=torch.float32, tiles=choice), c32), choice
     rows = sample_rows(M, w)
     qao, sao = oracle.quantize_1x128(f32(a_bits[rows]))
     idx = torch.from_numpy(rows).to(DEV)
@@ -711,8 +702,8 @@ def grouped_full_size(w):
     c32 = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32)
     c16 = T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.bfloat16)
     # the other tile shape of the exact path gives the same bits
-    with tiles("narrow" if M > 64 * G else "wide"):
-        assert torch.equal(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32), c32)
+    other = "narrow" if M > 64 * G else "wide"
+    assert torch.equal(T.grouped_gemm(qa, sa, offs, qb, sb, out_dtype=torch.float32, tiles=other), c32)
     rng = np.random.default_rng(44)
     for e in range(G):
         r0, r1 = int(off[e]), int(off[e + 1])
