@@ -8,34 +8,44 @@ workload (bf16 activations ~N(0,1) with 0.1% x100 outliers, bf16 weights
   2. fp8_quantize_block    -- weights B [7168][7168] -> E4M3 128x128 blocks,
                               written transposed (K contiguous)
   3. fp8_gemm_blockscaled  -- C = A . B, FP32 promotion every 128 of K, bf16 out
-Inputs are resident in HBM before the timed region; several input/output
-sets are rotated so that the 256 MB Infinity Cache cannot hold a step's
-working set from one step to the next.
+Inputs are resident in HBM before the timed region; four input/output sets
+(1.2 GB) are rotated so that the 256 MB Infinity Cache cannot hold a step's
+working set from one step to the next.  Before the --warmup steps the step
+runs for --settle-ms of wall time (reported as clock_settle_ms): after the
+host-side setup the GPU has idled, and its clock needs tens of milliseconds
+of load to reach its steady state.
 
 Printed: one JSON line.  `value` is whole-step throughput in GEMM TFLOP/s
 (2 M N K per step / wall time per step, quantizers included).  Per-kernel
 times come from HIP events recorded on the launch stream around every
-launch inside the timed region; `roofline` is the GEMM's (the dominant
+launch inside the timed region.  `roofline` is the GEMM's (the dominant
 kernel): algorithmic 2 M N K flops per GEMM call / its mean time, against
-the dense peak of the matrix instruction it runs (BF16: the FP8 operands are
-converted exactly to BF16 in registers, because the FP8 matrix instruction
-truncates inside its 8-product groups).  On this shape one GEMM call is two
-back-to-back launches of the same kernel, on 256- and on 192-column tiles
-(4096 and 3072 of the 7168 columns); the events bracket both.
-`hbm_copy_context` times a plain 1 GiB device copy in the same run: the HBM
-rate a pure stream reaches here, beside which the quantizers' fractions of
-the published 8 TB/s are to be read.
+the dense FP8 MFMA peak that the metric names.  The default path runs its
+products on the BF16 matrix cores (the FP8 operands are converted exactly
+to BF16 in registers, because gfx950's FP8 matrix instruction truncates
+inside its 8-product groups), so its ceiling is the BF16 peak, half the FP8
+one; `frac_bf16_peak` states the fraction against that ceiling.  On this
+shape one GEMM call is two back-to-back launches of the same kernel, on
+256- and on 192-column tiles (4096 and 3072 of the 7168 columns); the
+events bracket both.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 200]
+Entries outside the step (other workloads, other scale rules and paths)
+each rotate at least 1 GiB of operand and output sets, and run for 100 ms
+before 20 timed calls.  `hbm_copy_context` times a plain 1 GiB device copy
+in the same run: the HBM rate a pure stream reaches here, beside which the
+quantizers' fractions of the published 8 TB/s are to be read.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 200] [--settle-ms 500]
     python bench.py --copy-calibration   # plain 1 GiB device copy, for the
                                          # HBM-counter scale factor
-    python bench.py --kernel gemm|e8m0   # one GEMM kernel alone on the same
+    python bench.py --kernel NAME        # one kernel alone on the workload's
                                          # operands, for counter profiles
 """
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import platform
 import sys
@@ -47,24 +57,30 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense BF16 MFMA (published)
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+ROTATE_BYTES = 1 << 30       # operand sets rotated by every entry outside the step
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_blockscaled_dense_4096x7168x7168_traffic.txt")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_x1_amd", "csrc", "gemm.hip")
+
+KERNELS = ["gemm", "e8m0", "quant1x128", "quant128x128", "requant128x1"]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # ~80 ms of untimed warmup: the clocks take tens of milliseconds to settle
-    # after the setup, and the first steps run up to 12% slower
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
+    p.add_argument("--settle-ms", type=float, default=500.0,
+                   help="wall time of steps run before the warmup steps (clock settling)")
+    p.add_argument("--sets", type=int, default=4, help="rotated input/output sets of the step")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel", choices=["gemm", "e8m0"],
-                   help="run only this GEMM on the workload's operands (default path, or the "
-                        "E8M0-scale path on power-of-two operands), --steps times after "
-                        "--warmup, and print its mean time (for counter profiles)")
+    p.add_argument("--no-extra", action="store_true",
+                   help="time only the step (no entries outside it)")
+    p.add_argument("--kernel", choices=KERNELS,
+                   help="run only this kernel on the workload's operands (the GEMM's default "
+                        "path, the E8M0-scale path on power-of-two operands, or one quantizer), "
+                        "rotating >= 1 GiB of operand sets, --steps times after --warmup, and "
+                        "print its mean time (for counter profiles)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (counter calibration)")
     return p.parse_args()
@@ -138,36 +154,26 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
-def kernel_only(args, M, N, K, st, stream, B):
-    """One GEMM kernel alone, repeated: the default path on the step's amax
-    operands, or the E8M0-scale path on power-of-two operands."""
-    import torch
-    G = K // 128
-    pow2 = args.kernel == "e8m0"
-    rule = B.FP8FG_SCALE_POW2 if pow2 else B.FP8FG_SCALE_AMAX
-    B.fp8_quantize_rowtile(st["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128, rule,
-                           st["qa"], K, st["sa"], 1, M, stream)
-    B.fp8_quantize_block(st["b"], B.FP8FG_BF16, K, N, N, rule, 1, st["qb"], K, st["sb"], N // 128, 1,
-                         stream)
-    flags = B.FP8FG_GEMM_E8M0_SCALES if pow2 else B.FP8FG_GEMM_DEFAULT
+def progress(msg):
+    """One line on stderr as each part of the run ends."""
+    print("[bench] %s" % msg, file=sys.stderr, flush=True)
 
-    def gemm():
-        B.fp8_gemm_blockscaled(M, N, K, st["qa"], K, st["sa"], 1, M, st["qb"], K, st["sb"], 1,
-                               N // 128, B.FP8FG_BSCALE_BLOCK128, st["c"], B.FP8FG_BF16, N, flags,
-                               stream)
 
-    for _ in range(args.warmup):
-        gemm()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        gemm()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    print(json.dumps({"kernel": args.kernel, "ms": round(ms, 4),
-                      "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}), flush=True)
+def nbytes(*ts):
+    return sum(t.numel() * t.element_size() for t in ts)
+
+
+def n_sets(set_bytes):
+    """Operand sets needed to rotate at least 1 GiB."""
+    return max(2, math.ceil(ROTATE_BYTES / max(set_bytes, 1)))
+
+
+def clones(d, n):
+    """n sets: d itself and n - 1 deep copies of its tensors."""
+    out = [d]
+    for _ in range(n - 1):
+        out.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in d.items()})
+    return out
 
 
 def main():
@@ -182,6 +188,7 @@ def main():
     import torch
 
     from fp8_fine_grained_x1_amd import binding, workloads
+    from fp8_fine_grained_x1_amd import tensors as T
 
     binding.lib()   # fails loudly if the HIP library is not built
     if not torch.cuda.is_available():
@@ -192,6 +199,7 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    B = binding
 
     wl = workloads.WORKLOADS[2]
     M, N, K = wl["M"], wl["N"], wl["K"]
@@ -202,42 +210,85 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     a0, b0 = to_dev(d["A"]), to_dev(d["B"])
-    sets = []
-    for i in range(args.sets):
-        a = a0 if i == 0 else a0.clone()
-        b = b0 if i == 0 else b0.clone()
-        sets.append(dict(
+    stream = torch.cuda.current_stream(dev)
+
+    def new_step_set(a, b):
+        return dict(
             a=a, b=b,
             qa=torch.empty((M, K), dtype=torch.uint8, device=dev),
             sa=torch.empty((G, M), dtype=torch.float32, device=dev),    # group-major
             qb=torch.empty((N, K), dtype=torch.uint8, device=dev),
             sb=torch.empty((G, N // 128), dtype=torch.float32, device=dev),
-            c=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
-    stream = torch.cuda.current_stream(dev)
-    B = binding
+            c=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+
+    def quant_a(st, rule=B.FP8FG_SCALE_AMAX):
+        # sa(m, g) = sa[g * M + m]
+        B.fp8_quantize_rowtile(st["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128,
+                               rule, st["qa"], K, st["sa"], 1, M, stream)
+
+    def quant_b(st, rule=B.FP8FG_SCALE_AMAX):
+        B.fp8_quantize_block(st["b"], B.FP8FG_BF16, K, N, N, rule, 1, st["qb"], K,
+                             st["sb"], N // 128, 1, stream)
+
+    def gemm(st, flags=B.FP8FG_GEMM_DEFAULT, c=None):
+        B.fp8_gemm_blockscaled(M, N, K, st["qa"], K, st["sa"], 1, M, st["qb"], K,
+                               st["sb"], 1, N // 128, B.FP8FG_BSCALE_BLOCK128,
+                               st["c"] if c is None else c,
+                               B.FP8FG_BF16 if c is None or c.dtype == torch.bfloat16 else B.FP8FG_F32,
+                               N, flags, stream)
+
+    def requant(st):
+        B.fp8_quantize_rowtile(st["qa"], B.FP8FG_E4M3, M, K, K, st["sa"], 1, M,
+                               B.FP8FG_TILE_128x1, B.FP8FG_SCALE_AMAX, st["q2"], M, st["s2"], 1, K,
+                               stream)
+
+    def timed(fns, reps=20, warm_s=0.1):
+        """Mean HIP-event time of one call, cycling over the operand sets of
+        fns; the calls first run for warm_s of wall time (clock settling)."""
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < warm_s:
+            for _ in range(4):
+                fns[i % len(fns)]()
+                i += 1
+            torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            ev[2 * r].record(stream)
+            fns[r % len(fns)]()
+            ev[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps)]))
 
     if args.kernel:
-        kernel_only(args, M, N, K, sets[0], stream, B)
+        kernel_only(args, locals())
         return
+
+    sets = [new_step_set(a0 if i == 0 else a0.clone(), b0 if i == 0 else b0.clone())
+            for i in range(args.sets)]
 
     def step(st, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        # sa(m, g) = sa[g * M + m]
-        B.fp8_quantize_rowtile(st["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128,
-                               B.FP8FG_SCALE_AMAX, st["qa"], K, st["sa"], 1, M, stream)
+        quant_a(st)
         if ev is not None:
             ev[1].record(stream)
-        B.fp8_quantize_block(st["b"], B.FP8FG_BF16, K, N, N, B.FP8FG_SCALE_AMAX, 1, st["qb"], K,
-                             st["sb"], N // 128, 1, stream)
+        quant_b(st)
         if ev is not None:
             ev[2].record(stream)
-        B.fp8_gemm_blockscaled(M, N, K, st["qa"], K, st["sa"], 1, M, st["qb"], K,
-                               st["sb"], 1, N // 128, B.FP8FG_BSCALE_BLOCK128, st["c"],
-                               B.FP8FG_BF16, N, B.FP8FG_GEMM_DEFAULT, stream)
+        gemm(st)
         if ev is not None:
             ev[3].record(stream)
 
+    # clock settling, then the warmup steps as given, then the timed steps
+    t_settle = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step(sets[i % len(sets)])
+            i += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for i in range(args.warmup):
         step(sets[i % len(sets)])
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -247,175 +298,8 @@ def main():
         step(sets[i % len(sets)], events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
     ms_step = (t1 - t0) * 1e3 / args.steps
-
-    # Quantizer variants outside the step (same activations): the backward-pass
-    # 128x1 requantization of the FP8 activations (output transposed) and the
-    # power-of-two 1x128 rule.
-    st0 = sets[0]
-    q2 = torch.empty((K, M), dtype=torch.uint8, device=dev)
-    s2 = torch.empty((M // 128, K), dtype=torch.float32, device=dev)      # group-major
-    qp = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sp = torch.empty((G, M), dtype=torch.float32, device=dev)
-
-    def requant():
-        B.fp8_quantize_rowtile(st0["qa"], B.FP8FG_E4M3, M, K, K, st0["sa"], 1, M,
-                               B.FP8FG_TILE_128x1, B.FP8FG_SCALE_AMAX, q2, M, s2, 1, K, stream)
-
-    def pow2():
-        B.fp8_quantize_rowtile(st0["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128,
-                               B.FP8FG_SCALE_POW2, qp, K, sp, 1, M, stream)
-
-    def timed(fn, reps=20, warm_s=0.1):
-        # After the host-side setup of a workload the GPU has idled for
-        # seconds, and its clock needs tens of milliseconds of load to come
-        # back: run the call for warm_s of wall time before timing it.
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < warm_s:
-            for _ in range(4):
-                fn()
-            torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
-        for i in range(reps):
-            ev[2 * i].record(stream)
-            fn()
-            ev[2 * i + 1].record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)]))
-
-    rq_ms = timed(requant)
-    p2_ms = timed(pow2)
-
-    # The E8M0-scale path (FP8 MFMA dequantizing with power-of-two scales) on
-    # the same operands quantized with the power-of-two rule.
-    qa2 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa2 = torch.empty((G, M), dtype=torch.float32, device=dev)
-    qb2 = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    sb2 = torch.empty((G, N // 128), dtype=torch.float32, device=dev)
-    c2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    B.fp8_quantize_rowtile(st0["a"], B.FP8FG_BF16, M, K, K, None, 0, 0, B.FP8FG_TILE_1x128,
-                           B.FP8FG_SCALE_POW2, qa2, K, sa2, 1, M, stream)
-    B.fp8_quantize_block(st0["b"], B.FP8FG_BF16, K, N, N, B.FP8FG_SCALE_POW2, 1, qb2, K,
-                         sb2, N // 128, 1, stream)
-
-    def e8m0_gemm():
-        B.fp8_gemm_blockscaled(M, N, K, qa2, K, sa2, 1, M, qb2, K, sb2, 1, N // 128,
-                               B.FP8FG_BSCALE_BLOCK128, c2, B.FP8FG_BF16, N,
-                               B.FP8FG_GEMM_E8M0_SCALES, stream)
-
-    mx_ms = timed(e8m0_gemm)
-    del qa2, sa2, qb2, sb2, c2
-
-    # The same path on the step's own operands (amax scales, as the workload
-    # states): the scales' mantissas are applied in FP32.
-    def e8m0_gemm_amax():
-        B.fp8_gemm_blockscaled(M, N, K, st0["qa"], K, st0["sa"], 1, M, st0["qb"], K, st0["sb"], 1,
-                               N // 128, B.FP8FG_BSCALE_BLOCK128, st0["c"], B.FP8FG_BF16, N,
-                               B.FP8FG_GEMM_E8M0_SCALES, stream)
-
-    mxa_ms = timed(e8m0_gemm_amax)
-
-    # Dgrad of a layer of the same shape, dX [M][K] = dY [M][N] . W^T: dY
-    # quantized 1x128 along N, W [K][N] block-quantized without the transpose
-    # (its rows, the output columns, are then contraction-contiguous).
-    d6 = workloads.workload_inputs(6)
-    dy6, w6 = to_dev(d6["dY"]), to_dev(d6["W"])
-    qdy6 = torch.empty((M, N), dtype=torch.uint8, device=dev)
-    sdy6 = torch.empty((N // 128, M), dtype=torch.float32, device=dev)       # group-major
-    qw6 = torch.empty((K, N), dtype=torch.uint8, device=dev)
-    sw6 = torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev)
-    c6 = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    B.fp8_quantize_rowtile(dy6, B.FP8FG_BF16, M, N, N, None, 0, 0, B.FP8FG_TILE_1x128,
-                           B.FP8FG_SCALE_AMAX, qdy6, N, sdy6, 1, M, stream)
-    B.fp8_quantize_block(w6, B.FP8FG_BF16, K, N, N, B.FP8FG_SCALE_AMAX, 0, qw6, N,
-                         sw6, N // 128, 1, stream)
-    del dy6, w6
-
-    def dgrad():
-        B.fp8_gemm_blockscaled(M, K, N, qdy6, N, sdy6, 1, M, qw6, N, sw6, N // 128, 1,
-                               B.FP8FG_BSCALE_BLOCK128, c6, B.FP8FG_BF16, K, B.FP8FG_GEMM_DEFAULT,
-                               stream)
-
-    dg_ms = timed(dgrad)
-    del qdy6, sdy6, qw6, sw6, c6
-
-    def grouped_setup(w):
-        """FP8 operands of a grouped workload: 1x128 power-of-two activation
-        scales (group-major), per-expert 128x128 weight blocks, transposed."""
-        dw = workloads.workload_inputs(w)
-        spec = workloads.WORKLOADS[w]
-        Gx, Mx, Nx, Kx = spec["G"], spec["M"], spec["N"], spec["K"]
-        ax = to_dev(dw["A"])
-        o = dict(G=Gx, M=Mx, N=Nx, K=Kx,
-                 qa=torch.empty((Mx, Kx), dtype=torch.uint8, device=dev),
-                 sa=torch.empty((Kx // 128, Mx), dtype=torch.float32, device=dev),
-                 qb=torch.empty((Gx, Nx, Kx), dtype=torch.uint8, device=dev),
-                 sb=torch.empty((Gx, Kx // 128, Nx // 128), dtype=torch.float32, device=dev),
-                 c=torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev),
-                 off=torch.from_numpy(dw["offsets"].astype(np.int32)).to(dev),
-                 counts=dw["counts"].tolist())
-        B.fp8_quantize_rowtile(ax, B.FP8FG_BF16, Mx, Kx, Kx, None, 0, 0, B.FP8FG_TILE_1x128,
-                               B.FP8FG_SCALE_POW2, o["qa"], Kx, o["sa"], 1, Mx, stream)
-        for e in range(Gx):
-            we = to_dev(dw["W"][e])
-            B.fp8_quantize_block(we, B.FP8FG_BF16, Kx, Nx, Nx, B.FP8FG_SCALE_AMAX, 1, o["qb"][e], Kx,
-                                 o["sb"][e], Nx // 128, 1, stream)
-        torch.cuda.synchronize()
-        return o
-
-    def grouped(o):
-        B.fp8_grouped_gemm_blockscaled(o["G"], o["off"], o["M"], o["N"], o["K"], o["qa"], o["K"],
-                                       o["sa"], 1, o["M"], o["qb"], o["K"], o["N"] * o["K"], o["sb"],
-                                       1, o["N"] // 128, (o["K"] // 128) * (o["N"] // 128), o["c"],
-                                       B.FP8FG_BF16, o["N"], B.FP8FG_GEMM_DEFAULT, stream)
-
-    g4 = grouped_setup(4)
-    up_ms = timed(lambda: grouped(g4))
-    up_flops = 2.0 * g4["M"] * g4["N"] * g4["K"]
-    del g4
-    g7 = grouped_setup(7)
-    dn_ms = timed(lambda: grouped(g7))
-    dn_flops = 2.0 * g7["M"] * g7["N"] * g7["K"]
-    del g7
-    g8 = grouped_setup(8)
-    dc_ms = timed(lambda: grouped(g8))
-    dc_flops = 2.0 * g8["M"] * g8["N"] * g8["K"]
-    # algorithmic bytes of the decode call: every expert's weights and block
-    # scales once, the activations and their scales once, the bf16 output once
-    dc_bytes = (g8["G"] * g8["N"] * g8["K"] + g8["G"] * (g8["K"] // 128) * (g8["N"] // 128) * 4
-                + g8["M"] * g8["K"] + g8["M"] * (g8["K"] // 128) * 4 + g8["M"] * g8["N"] * 2)
-    dc_desc = "G=%d, %d tokens (%d-%d per expert), K=%d -> N=%d" % (
-        g8["G"], g8["M"], min(g8["counts"]), max(g8["counts"]), g8["K"], g8["N"])
-    del g8
-    # Long-K dense GEMM (1024 x 4096 x 16384: 128 promotions per output).
-    from fp8_fine_grained_x1_amd import tensors as T
-    w3 = workloads.WORKLOADS[3]
-    d3 = workloads.workload_inputs(3)
-    qa3, sa3 = T.quantize_1x128(to_dev(d3["A"]))
-    qb3, sb3 = T.quantize_block(to_dev(d3["B"]))
-    c3 = torch.empty((w3["M"], w3["N"]), dtype=torch.bfloat16, device=dev)
-    lk_ms = timed(lambda: T.gemm(qa3, sa3, qb3, sb3, out=c3))
-    lk_flops = 2.0 * w3["M"] * w3["N"] * w3["K"]
-    del d3, qa3, sa3, qb3, sb3, c3
-    # Weight gradient dW [F][N] = X^T dY over T = 8192 tokens: X and dY
-    # quantized 1x128, requantized to 128x1 tiles (transposed, per-column
-    # scales along the token axis), FP32 out.
-    w5 = workloads.WORKLOADS[5]
-    d5 = workloads.workload_inputs(5)
-    qx5, sx5 = T.requantize_128x1(*T.quantize_1x128(to_dev(d5["X"])))
-    qd5, sd5 = T.requantize_128x1(*T.quantize_1x128(to_dev(d5["dY"])))
-    c5 = torch.empty((w5["F"], w5["N"]), dtype=torch.float32, device=dev)
-    wg_ms = timed(lambda: T.gemm(qx5, sx5, qd5, sd5, out=c5, col_scales=True))
-    wg_flops = 2.0 * w5["F"] * w5["N"] * w5["T"]
-    del d5, qx5, sx5, qd5, sd5, c5
-
-    # Context for the HBM fractions: a plain 1 GiB device-to-device copy (the
-    # runtime's copy kernel) in the same run, read + write bytes per time.
-    cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-    cp_dst = torch.empty_like(cp_src)
-    cp_ms = timed(lambda: cp_dst.copy_(cp_src), reps=10)
-    del cp_src, cp_dst
+    progress("step timed: %.4f ms per step after %.0f ms of clock settling" % (ms_step, settle_ms))
 
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
@@ -427,11 +311,41 @@ def main():
     bytes_rq = M * K * (1 + 1) + M * G * 4 + (M // 128) * K * 4
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
 
-    def gbs(nbytes, ms):
-        return nbytes / (ms * 1e-3) / 1e9
+    def gbs(nb, ms):
+        return nb / (ms * 1e-3) / 1e9
 
-    def tflops(nflops, ms):
-        return nflops / (ms * 1e-3) / 1e12
+    def tflops(nf, ms):
+        return nf / (ms * 1e-3) / 1e12
+
+    def q_entry(nb, ms, sets_n):
+        return {"ms": round(ms, 4), "GB/s": round(gbs(nb, ms), 1),
+                "frac_hbm": round(gbs(nb, ms) / PEAK_HBM_GBS, 3), "rotated_sets": sets_n}
+
+    def g_entry(nf, ms, sets_n, peak=PEAK_BF16_TFLOPS, **extra):
+        e = {"ms": round(ms, 4), "TFLOP/s": round(tflops(nf, ms), 1),
+             "frac_fp8_peak": round(tflops(nf, ms) / PEAK_FP8_TFLOPS, 4)}
+        if peak == PEAK_BF16_TFLOPS:
+            e["frac_bf16_peak"] = round(tflops(nf, ms) / PEAK_BF16_TFLOPS, 4)
+        e["rotated_sets"] = sets_n
+        e.update(extra)
+        return e
+
+    kernels = {
+        "fp8_quantize_rowtile_1x128": {
+            "ms": round(qa_ms, 4), "GB/s": round(gbs(bytes_qa, qa_ms), 1),
+            "frac_hbm": round(gbs(bytes_qa, qa_ms) / PEAK_HBM_GBS, 3)},
+        "fp8_quantize_block_128x128": {
+            "ms": round(qb_ms, 4), "GB/s": round(gbs(bytes_qb, qb_ms), 1),
+            "frac_hbm": round(gbs(bytes_qb, qb_ms) / PEAK_HBM_GBS, 3)},
+        "fp8_gemm_blockscaled": {
+            "ms": round(gemm_ms, 4), "TFLOP/s": round(gemm_tflops, 1),
+            "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
+    }
+    extra = {}
+    if not args.no_extra:
+        extra = outside_step(locals())
+        kernels.update(extra.pop("kernels"))
 
     out = {
         "metric": "block-scaled FP8 GEMM TFLOPS (% FP8 MFMA peak); quantize GB/s (% HBM)",
@@ -440,6 +354,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_ms": round(settle_ms, 1),
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -449,66 +364,327 @@ def main():
         "config": {"workload": "dense forward GEMM 4096x7168x7168, 1x128 activation tiles, "
                                "128x128 weight blocks, bf16 out (quantize A + quantize B + GEMM)",
                    "M": M, "N": N, "K": K, "parallelism": "single GPU"},
-        "kernels": {
-            "fp8_quantize_rowtile_1x128": {
-                "ms": round(qa_ms, 4), "GB/s": round(gbs(bytes_qa, qa_ms), 1),
-                "frac_hbm": round(gbs(bytes_qa, qa_ms) / PEAK_HBM_GBS, 3)},
-            "fp8_quantize_block_128x128": {
-                "ms": round(qb_ms, 4), "GB/s": round(gbs(bytes_qb, qb_ms), 1),
-                "frac_hbm": round(gbs(bytes_qb, qb_ms) / PEAK_HBM_GBS, 3)},
-            "fp8_quantize_rowtile_128x1_requant (outside the step)": {
-                "ms": round(rq_ms, 4), "GB/s": round(gbs(bytes_rq, rq_ms), 1),
-                "frac_hbm": round(gbs(bytes_rq, rq_ms) / PEAK_HBM_GBS, 3)},
-            "fp8_quantize_rowtile_1x128_pow2 (outside the step)": {
-                "ms": round(p2_ms, 4), "GB/s": round(gbs(bytes_qa, p2_ms), 1),
-                "frac_hbm": round(gbs(bytes_qa, p2_ms) / PEAK_HBM_GBS, 3)},
-            "fp8_gemm_blockscaled": {
-                "ms": round(gemm_ms, 4), "TFLOP/s": round(gemm_tflops, 1),
-                "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
-            "fp8_gemm_blockscaled E8M0_SCALES (FP8 MFMA dequantizing; pow2 scales), "
-            "4096x7168x7168 (outside the step)": {
-                "ms": round(mx_ms, 4), "TFLOP/s": round(tflops(flops, mx_ms), 1),
-                "frac_fp8_peak": round(tflops(flops, mx_ms) / PEAK_FP8_TFLOPS, 4)},
-            "fp8_gemm_blockscaled E8M0_SCALES (FP8 MFMA dequantizing; amax scales, the step's "
-            "operands), 4096x7168x7168 (outside the step)": {
-                "ms": round(mxa_ms, 4), "TFLOP/s": round(tflops(flops, mxa_ms), 1),
-                "frac_fp8_peak": round(tflops(flops, mxa_ms) / PEAK_FP8_TFLOPS, 4)},
-            "fp8_gemm_blockscaled dgrad dX = dY.W^T, 4096x7168x7168 (outside the step)": {
-                "ms": round(dg_ms, 4), "TFLOP/s": round(tflops(flops, dg_ms), 1),
-                "frac_bf16_peak": round(tflops(flops, dg_ms) / PEAK_BF16_TFLOPS, 4)},
-            "fp8_gemm_blockscaled long K 1024x4096x16384 (outside the step)": {
-                "ms": round(lk_ms, 4), "TFLOP/s": round(tflops(lk_flops, lk_ms), 1),
-                "frac_bf16_peak": round(tflops(lk_flops, lk_ms) / PEAK_BF16_TFLOPS, 4)},
-            "fp8_gemm_blockscaled wgrad dW = X^T.dY 7168x4096, 8192 tokens, 128x1 column scales, "
-            "f32 out (outside the step)": {
-                "ms": round(wg_ms, 4), "TFLOP/s": round(tflops(wg_flops, wg_ms), 1),
-                "frac_bf16_peak": round(tflops(wg_flops, wg_ms) / PEAK_BF16_TFLOPS, 4)},
-            "fp8_grouped_gemm_blockscaled MoE up-projection G=8, 16384 tokens, K=7168 -> N=4096, "
-            "pow2 activation scales (outside the step)": {
-                "ms": round(up_ms, 4), "TFLOP/s": round(tflops(up_flops, up_ms), 1),
-                "frac_bf16_peak": round(tflops(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4)},
-            "fp8_grouped_gemm_blockscaled MoE down-projection G=8, 16384 tokens, K=4096 -> N=7168, "
-            "pow2 activation scales (outside the step)": {
-                "ms": round(dn_ms, 4), "TFLOP/s": round(tflops(dn_flops, dn_ms), 1),
-                "frac_bf16_peak": round(tflops(dn_flops, dn_ms) / PEAK_BF16_TFLOPS, 4)},
-            "fp8_grouped_gemm_blockscaled MoE decode %s (outside the step)" % dc_desc: {
-                "ms": round(dc_ms, 4), "GB/s": round(gbs(dc_bytes, dc_ms), 1),
-                "frac_hbm": round(gbs(dc_bytes, dc_ms) / PEAK_HBM_GBS, 3),
-                "TFLOP/s": round(tflops(dc_flops, dc_ms), 1)},
-        },
-        "hbm_copy_context": {
-            "1 GiB device copy GB/s (read + write)": round(gbs(2 * (1 << 30), cp_ms), 1),
-            "frac_hbm": round(gbs(2 * (1 << 30), cp_ms) / PEAK_HBM_GBS, 3)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile()},
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic_from_profile(),
+                     "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "ceiling_frac_of_fp8_peak": PEAK_BF16_TFLOPS / PEAK_FP8_TFLOPS,
+                     "note": "the default path multiplies on the BF16 matrix cores (exact "
+                             "products); traffic is HBM bytes per GEMM call from the committed "
+                             "counter profile of the same kernel source (null otherwise)"},
         "context": "the pages report no throughput; their only figure is ~2% max relative error "
                    "of un-promoted FP8 accumulation at K=4096 on Hopper",
     }
+    out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d["A"], d["B"])
+        progress("cpu baseline done")
     print(json.dumps(out), flush=True)
+
+
+def outside_step(env):
+    """Entries outside the step, each on >= 1 GiB of rotated operand sets;
+    returns {"kernels": {...}, "hbm_copy_context": ..., "error_context": ...}."""
+    import numpy as np
+    import torch
+
+    from fp8_fine_grained_x1_amd import binding as B
+    from fp8_fine_grained_x1_amd import tensors as T
+    from fp8_fine_grained_x1_amd import workloads
+
+    dev, stream, M, N, K, G = env["dev"], env["stream"], env["M"], env["N"], env["K"], env["G"]
+    to_dev, timed, gemm, requant = env["to_dev"], env["timed"], env["gemm"], env["requant"]
+    quant_a, quant_b, new_step_set = env["quant_a"], env["quant_b"], env["new_step_set"]
+    gbs, tflops, q_entry, g_entry = env["gbs"], env["tflops"], env["q_entry"], env["g_entry"]
+    st0 = env["sets"][0]
+    flops, bytes_qa, bytes_rq = env["flops"], env["bytes_qa"], env["bytes_rq"]
+    kernels = {}
+
+    def rel_err(c, ref):
+        """rel_frob and max_rel (|ref| > 1e-2 rms(ref)) in float64 on the GPU."""
+        c = c.to(torch.float64)
+        ref = ref.to(torch.float64)
+        fro = float(torch.linalg.norm(c - ref) / torch.linalg.norm(ref))
+        mask = ref.abs() > 1e-2 * torch.sqrt(torch.mean(ref * ref))
+        mr = float(((c - ref).abs()[mask] / ref.abs()[mask]).max())
+        return fro, mr
+
+    # ---- 128x1 requantization of the step's FP8 activations (transposed out)
+    base = dict(qa=st0["qa"].clone(), sa=st0["sa"].clone(),
+                q2=torch.empty((K, M), dtype=torch.uint8, device=dev),
+                s2=torch.empty((M // 128, K), dtype=torch.float32, device=dev))
+    rs = clones(base, n_sets(nbytes(*base.values())))
+    ms = timed([lambda s=s: requant(s) for s in rs])
+    kernels["fp8_quantize_rowtile_128x1_requant (outside the step)"] = q_entry(bytes_rq, ms, len(rs))
+    progress("requant 128x1 timed")
+    del rs, base
+
+    # ---- power-of-two 1x128 rule on the step's activations
+    base = dict(a=st0["a"], qa=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                sa=torch.empty((G, M), dtype=torch.float32, device=dev))
+    ps = clones(base, n_sets(nbytes(*base.values())))
+    ms = timed([lambda s=s: quant_a(s, B.FP8FG_SCALE_POW2) for s in ps])
+    kernels["fp8_quantize_rowtile_1x128_pow2 (outside the step)"] = q_entry(bytes_qa, ms, len(ps))
+    progress("pow2 1x128 timed")
+    del ps, base
+
+    # ---- E8M0-scale path (FP8 MFMA dequantizing): power-of-two operands, and
+    # the step's own amax operands; error against the exact default path's
+    # FP32 result on the same operands (which matches the oracle to ~1e-7)
+    for label, rule in (("pow2 scales", B.FP8FG_SCALE_POW2), ("amax scales, the step's operands",
+                                                                B.FP8FG_SCALE_AMAX)):
+        base = new_step_set(st0["a"], st0["b"])
+        quant_a(base, rule)
+        quant_b(base, rule)
+        del base["a"], base["b"]
+        c_mx = torch.empty((M, N), dtype=torch.float32, device=dev)
+        c_ex = torch.empty((M, N), dtype=torch.float32, device=dev)
+        gemm(base, B.FP8FG_GEMM_E8M0_SCALES, c_mx)
+        gemm(base, B.FP8FG_GEMM_DEFAULT, c_ex)
+        fro, mr = rel_err(c_mx, c_ex)
+        del c_mx, c_ex
+        gs = clones(base, n_sets(nbytes(*base.values())))
+        ms = timed([lambda s=s: gemm(s, B.FP8FG_GEMM_E8M0_SCALES) for s in gs])
+        kernels["fp8_gemm_blockscaled E8M0_SCALES (FP8 MFMA dequantizing; %s), 4096x7168x7168 "
+                "(outside the step)" % label] = g_entry(
+            flops, ms, len(gs), peak=PEAK_FP8_TFLOPS,
+            rel_frob_vs_exact_path=float("%.3e" % fro), max_rel_vs_exact_path=float("%.3e" % mr))
+        progress("E8M0 GEMM (%s) timed" % label)
+        del gs, base
+
+    # ---- Dgrad dX [M][K] = dY [M][N] . W^T of a layer of the same shape: dY
+    # quantized 1x128 along N, W [K][N] block-quantized without the transpose
+    d6 = workloads.workload_inputs(6)
+    dy6, w6 = to_dev(d6["dY"]), to_dev(d6["W"])
+    base = dict(qd=torch.empty((M, N), dtype=torch.uint8, device=dev),
+                sd=torch.empty((N // 128, M), dtype=torch.float32, device=dev),
+                qw=torch.empty((K, N), dtype=torch.uint8, device=dev),
+                sw=torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev),
+                c=torch.empty((M, K), dtype=torch.bfloat16, device=dev))
+    B.fp8_quantize_rowtile(dy6, B.FP8FG_BF16, M, N, N, None, 0, 0, B.FP8FG_TILE_1x128,
+                           B.FP8FG_SCALE_AMAX, base["qd"], N, base["sd"], 1, M, stream)
+    B.fp8_quantize_block(w6, B.FP8FG_BF16, K, N, N, B.FP8FG_SCALE_AMAX, 0, base["qw"], N,
+                         base["sw"], N // 128, 1, stream)
+    del dy6, w6, d6
+
+    def dgrad(s):
+        B.fp8_gemm_blockscaled(M, K, N, s["qd"], N, s["sd"], 1, M, s["qw"], N, s["sw"], N // 128, 1,
+                               B.FP8FG_BSCALE_BLOCK128, s["c"], B.FP8FG_BF16, K,
+                               B.FP8FG_GEMM_DEFAULT, stream)
+
+    gs = clones(base, n_sets(nbytes(*base.values())))
+    ms = timed([lambda s=s: dgrad(s) for s in gs])
+    kernels["fp8_gemm_blockscaled dgrad dX = dY.W^T, 4096x7168x7168 (outside the step)"] = g_entry(
+        flops, ms, len(gs))
+    progress("dgrad timed")
+    del gs, base
+
+    # ---- grouped GEMMs (MoE): power-of-two 1x128 activation scales
+    # (group-major), per-expert 128x128 weight blocks, transposed
+    def grouped_setup(w):
+        dw = workloads.workload_inputs(w)
+        spec = workloads.WORKLOADS[w]
+        Gx, Mx, Nx, Kx = spec["G"], spec["M"], spec["N"], spec["K"]
+        ax = to_dev(dw["A"])
+        o = dict(qa=torch.empty((Mx, Kx), dtype=torch.uint8, device=dev),
+                 sa=torch.empty((Kx // 128, Mx), dtype=torch.float32, device=dev),
+                 qb=torch.empty((Gx, Nx, Kx), dtype=torch.uint8, device=dev),
+                 sb=torch.empty((Gx, Kx // 128, Nx // 128), dtype=torch.float32, device=dev),
+                 c=torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev),
+                 off=torch.from_numpy(dw["offsets"].astype(np.int32)).to(dev))
+        B.fp8_quantize_rowtile(ax, B.FP8FG_BF16, Mx, Kx, Kx, None, 0, 0, B.FP8FG_TILE_1x128,
+                               B.FP8FG_SCALE_POW2, o["qa"], Kx, o["sa"], 1, Mx, stream)
+        for e in range(Gx):
+            we = to_dev(dw["W"][e])
+            B.fp8_quantize_block(we, B.FP8FG_BF16, Kx, Nx, Nx, B.FP8FG_SCALE_AMAX, 1, o["qb"][e], Kx,
+                                 o["sb"][e], Nx // 128, 1, stream)
+        torch.cuda.synchronize()
+        meta = dict(G=Gx, M=Mx, N=Nx, K=Kx, counts=dw["counts"].tolist())
+        return o, meta
+
+    def grouped(o, m):
+        B.fp8_grouped_gemm_blockscaled(m["G"], o["off"], m["M"], m["N"], m["K"], o["qa"], m["K"],
+                                       o["sa"], 1, m["M"], o["qb"], m["K"], m["N"] * m["K"], o["sb"],
+                                       1, m["N"] // 128, (m["K"] // 128) * (m["N"] // 128), o["c"],
+                                       B.FP8FG_BF16, m["N"], B.FP8FG_GEMM_DEFAULT, stream)
+
+    for w, label in ((4, "MoE up-projection G=8, 16384 tokens, K=7168 -> N=4096, pow2 activation "
+                         "scales"),
+                     (7, "MoE down-projection G=8, 16384 tokens, K=4096 -> N=7168, pow2 activation "
+                         "scales"),
+                     (8, None)):
+        o, m = grouped_setup(w)
+        gs = clones(o, n_sets(nbytes(*o.values())))
+        ms = timed([lambda s=s: grouped(s, m) for s in gs])
+        nf = 2.0 * m["M"] * m["N"] * m["K"]
+        if label is not None:
+            kernels["fp8_grouped_gemm_blockscaled %s (outside the step)" % label] = g_entry(nf, ms, len(gs))
+        else:
+            # algorithmic bytes of the decode call: every expert's weights and
+            # block scales once, the activations and their scales once, the
+            # bf16 output once
+            nb = (m["G"] * m["N"] * m["K"] + m["G"] * (m["K"] // 128) * (m["N"] // 128) * 4
+                  + m["M"] * m["K"] + m["M"] * (m["K"] // 128) * 4 + m["M"] * m["N"] * 2)
+            desc = "G=%d, %d tokens (%d-%d per expert), K=%d -> N=%d" % (
+                m["G"], m["M"], min(m["counts"]), max(m["counts"]), m["K"], m["N"])
+            e = q_entry(nb, ms, len(gs))
+            e["TFLOP/s"] = round(tflops(nf, ms), 1)
+            kernels["fp8_grouped_gemm_blockscaled MoE decode %s (outside the step)" % desc] = e
+        progress("grouped workload %d timed" % w)
+        del gs, o
+
+    # ---- long-K dense GEMM (1024 x 4096 x 16384: 128 promotions per output)
+    w3 = workloads.WORKLOADS[3]
+    d3 = workloads.workload_inputs(3)
+    a3, b3 = to_dev(d3["A"]), to_dev(d3["B"])
+    qa3, sa3 = T.quantize_1x128(a3)
+    qb3, sb3 = T.quantize_block(b3)
+    base = dict(qa=qa3, sa=sa3, qb=qb3, sb=sb3,
+                c=torch.empty((w3["M"], w3["N"]), dtype=torch.bfloat16, device=dev))
+    gs = clones(base, n_sets(nbytes(*base.values())))
+    ms = timed([lambda s=s: T.gemm(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"]) for s in gs])
+    kernels["fp8_gemm_blockscaled long K 1024x4096x16384 (outside the step)"] = g_entry(
+        2.0 * w3["M"] * w3["N"] * w3["K"], ms, len(gs))
+    del gs
+    progress("long K timed")
+    error_context = long_k_error_gap(a3, b3, qa3, sa3, qb3, sb3, rel_err)
+    progress("long-K error gap measured")
+    del base, qa3, sa3, qb3, sb3, a3, b3, d3
+
+    # ---- weight gradient dW [F][N] = X^T dY over T = 8192 tokens: X and dY
+    # quantized 1x128, requantized to 128x1 tiles (transposed, per-column
+    # scales along the token axis), FP32 out
+    w5 = workloads.WORKLOADS[5]
+    d5 = workloads.workload_inputs(5)
+    qx5, sx5 = T.requantize_128x1(*T.quantize_1x128(to_dev(d5["X"])))
+    qd5, sd5 = T.requantize_128x1(*T.quantize_1x128(to_dev(d5["dY"])))
+    base = dict(qx=qx5, sx=sx5, qd=qd5, sd=sd5,
+                c=torch.empty((w5["F"], w5["N"]), dtype=torch.float32, device=dev))
+    gs = clones(base, n_sets(nbytes(*base.values())))
+    ms = timed([lambda s=s: T.gemm(s["qx"], s["sx"], s["qd"], s["sd"], out=s["c"], col_scales=True)
+                for s in gs])
+    kernels["fp8_gemm_blockscaled wgrad dW = X^T.dY 7168x4096, 8192 tokens, 128x1 column scales, "
+            "f32 out (outside the step)"] = g_entry(2.0 * w5["F"] * w5["N"] * w5["T"], ms, len(gs))
+    progress("wgrad timed")
+    del gs, base, qx5, sx5, qd5, sd5, d5
+
+    # ---- context: a plain 1 GiB device-to-device copy (the runtime's copy
+    # kernel), read + write bytes per time
+    cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    cp_dst = torch.empty_like(cp_src)
+    cp_ms = timed([lambda: cp_dst.copy_(cp_src)], reps=10)
+    del cp_src, cp_dst
+    return {
+        "kernels": kernels,
+        "hbm_copy_context": {
+            "1 GiB device copy GB/s (read + write)": round(gbs(2 * (1 << 30), cp_ms), 1),
+            "frac_hbm": round(gbs(2 * (1 << 30), cp_ms) / PEAK_HBM_GBS, 3)},
+        "error_context": error_context,
+    }
+
+
+def long_k_error_gap(a3, b3, qa3, sa3, qb3, sb3, rel_err):
+    """Long-K workload (1024 x 4096 x 16384, U(-1,1)): the fine-grained path
+    (1x128 / 128x128 scales, exact partial sums promoted every 128 of K) and
+    the naive baseline (per-tensor scales, the whole K summed in the FP8
+    matrix core, no promotion) against the unquantized product, and the
+    naive path against the exact product of its own E4M3 operands (its
+    accumulation error alone).  64 sampled rows, all 4096 columns, float64
+    references on the GPU.  The per-tensor operands are prepared here, as a
+    harness would (scale = tensor amax / 448, E4M3 by torch's cast)."""
+    import torch
+
+    from fp8_fine_grained_x1_amd import binding as B
+    from fp8_fine_grained_x1_amd import tensors as T
+
+    M, Kx = a3.shape
+    N = b3.shape[1]
+    rows = torch.linspace(0, M - 1, 64, device=a3.device).round().long()
+    af, bf = a3.float(), b3.float()
+    s_a = (af.abs().max() / 448.0).reshape(1)
+    s_b = (bf.abs().max() / 448.0).reshape(1)
+    qa_n = (af / s_a).to(torch.float8_e4m3fn).view(torch.uint8)
+    qb_n = (bf / s_b).t().contiguous().to(torch.float8_e4m3fn).view(torch.uint8)   # [N][K]
+    naive = T.gemm(qa_n, s_a, qb_n, s_b, out_dtype=torch.float32, no_promotion=True)[rows]
+    fine = T.gemm(qa3, sa3, qb3, sb3, out_dtype=torch.float32)[rows]
+    truth = a3[rows].double() @ b3.double()
+    own = ((qa_n[rows].view(torch.float8_e4m3fn).double() * s_a.double()) @
+           (qb_n.view(torch.float8_e4m3fn).double().t().contiguous() * s_b.double()))
+    f_fro, f_mr = rel_err(fine, truth)
+    n_fro, n_mr = rel_err(naive, truth)
+    a_fro, a_mr = rel_err(naive, own)
+    torch.cuda.synchronize()
+    return {
+        "workload": "long-K 1024x4096x16384, U(-1,1); 64 sampled rows x 4096 columns",
+        "fine_grained_vs_unquantized": {"rel_frob": float("%.4e" % f_fro), "max_rel": float("%.4e" % f_mr)},
+        "naive_per_tensor_no_promotion_vs_unquantized": {"rel_frob": float("%.4e" % n_fro),
+                                                         "max_rel": float("%.4e" % n_mr)},
+        "naive_accumulation_vs_exact_product_of_its_operands": {"rel_frob": float("%.4e" % a_fro),
+                                                               "max_rel": float("%.4e" % a_mr)},
+        "pages_context": "~2% max relative error of limited-width FP8 accumulation at K=4096 "
+                         "(Hopper, preliminary test; no inputs given)",
+    }
+
+
+def kernel_only(args, env):
+    """One kernel alone, repeated over >= 1 GiB of rotated operand sets: the
+    GEMM's default path on the step's amax operands, the E8M0-scale path on
+    power-of-two operands, or one of the step's quantizers."""
+    import numpy as np
+    import torch
+
+    from fp8_fine_grained_x1_amd import binding as B
+
+    M, N, K = env["M"], env["N"], env["K"]
+    a0, b0 = env["a0"], env["b0"]
+    new_step_set, quant_a, quant_b = env["new_step_set"], env["quant_a"], env["quant_b"]
+    gemm, requant, stream = env["gemm"], env["requant"], env["stream"]
+    k = args.kernel
+    if k in ("gemm", "e8m0"):
+        rule = B.FP8FG_SCALE_POW2 if k == "e8m0" else B.FP8FG_SCALE_AMAX
+        base = new_step_set(a0, b0)
+        quant_a(base, rule)
+        quant_b(base, rule)
+        del base["a"], base["b"]
+        flags = B.FP8FG_GEMM_E8M0_SCALES if k == "e8m0" else B.FP8FG_GEMM_DEFAULT
+        sets = clones(base, n_sets(nbytes(*base.values())))
+        fn = lambda s: gemm(s, flags)
+        work = 2.0 * M * N * K
+    elif k == "quant1x128":
+        base = new_step_set(a0, b0)
+        del base["b"], base["qb"], base["sb"], base["c"]
+        sets = clones(base, n_sets(nbytes(*base.values())))
+        fn = quant_a
+        work = M * K * 3 + M * (K // 128) * 4
+    elif k == "quant128x128":
+        base = new_step_set(a0, b0)
+        del base["a"], base["qa"], base["sa"], base["c"]
+        sets = clones(base, n_sets(nbytes(*base.values())))
+        fn = quant_b
+        work = K * N * 3 + (K // 128) * (N // 128) * 4
+    else:
+        base = new_step_set(a0, b0)
+        quant_a(base)
+        base = dict(qa=base["qa"], sa=base["sa"],
+                    q2=torch.empty((K, M), dtype=torch.uint8, device=env["dev"]),
+                    s2=torch.empty((M // 128, K), dtype=torch.float32, device=env["dev"]))
+        sets = clones(base, n_sets(nbytes(*base.values())))
+        fn = requant
+        work = M * K * 2 + M * (K // 128) * 4 + (M // 128) * K * 4
+    for i in range(args.warmup):
+        fn(sets[i % len(sets)])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        fn(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    rate = ({"TFLOP/s": round(work / (ms * 1e-3) / 1e12, 1)} if k in ("gemm", "e8m0")
+            else {"GB/s": round(work / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": work})
+    print(json.dumps(dict(kernel=k, ms=round(ms, 4), rotated_sets=len(sets), **rate)), flush=True)
 
 
 if __name__ == "__main__":
