@@ -36,37 +36,65 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-// A tile's scale s (dequantization multiplier) and y = RN(1/s).
+// A tile's scale s (the stored dequantization multiplier) and what the
+// quotient x / s is formed from: x * pre divided by d = s * pre, with
+// y = RN(1/d).  pre is 1 unless s < 2^-64, where it is 2^64: with tiny
+// scales the residual of the FMA correction below falls into FP32's
+// denormal range and loses bits (the quotient of x ~ 1.4e-38 by
+// s ~ 2e-36 came out one ulp low), while the same quotient of the operands
+// scaled by 2^64 -- exactly, both being powers of two apart from s -- has a
+// normal residual whenever x / s is large enough to matter for E4M3
+// (>= 2^-11).
 struct TileScale {
   float s;
+  float d;
   float y;
+  float pre;
 };
 
-// s = max(RN(amax / 448), 2^-126); y = RN(1 / s).  Both divisions are the
-// compiler's correctly rounded fp32 division (no fast-math is used).
+constexpr float kTinyScale = 5.42101086242752217004e-20f;  // 2^-64
+constexpr float kTinyLift = 18446744073709551616.0f;        // 2^64
+
+// s = max(RN(amax / 448), 2^-126); the divisions are the compiler's
+// correctly rounded fp32 division (no fast-math is used).
 __device__ __forceinline__ TileScale scale_amax(float amax) {
-  float s = fmaxf(amax / kE4M3Max, kFltMinNormal);
-  return {s, 1.0f / s};
+  const float s = fmaxf(amax / kE4M3Max, kFltMinNormal);
+  const float pre = s < kTinyScale ? kTinyLift : 1.0f;
+  const float d = s * pre;
+  return {s, d, 1.0f / d, pre};
 }
 
 // s = max(2^k, 2^-126) with k the least integer such that 448 * 2^k >= amax.
 // With amax = 1.f * 2^e: amax / 448 = (1.f / 1.75) * 2^(e - 8), so
 // k = e - 8 when 1.f <= 1.75 (mantissa field <= 0x600000) and e - 7 otherwise.
-// Zero and subnormal amax fall below the floor.
+// Zero and subnormal amax fall below the floor.  x / s = x * 2^-k is exact
+// (or below the E4M3 range), so y = 2^-k is all the quotient needs.
 __device__ __forceinline__ TileScale scale_pow2(float amax) {
   const uint32_t u = __float_as_uint(amax);
   int k = (int)((u >> 23) & 0xFFu) - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
   k = k < -126 ? -126 : k;
-  return {__uint_as_float((uint32_t)(k + 127) << 23), __uint_as_float((uint32_t)(127 - k) << 23)};
+  const float s = __uint_as_float((uint32_t)(k + 127) << 23);
+  return {s, s, __uint_as_float((uint32_t)(127 - k) << 23), 1.0f};
 }
 
-// Correctly rounded x / s from y = RN(1/s) (Markstein's FMA-based quotient
-// correction; P. Markstein, IBM J. Res. Dev. 34(1), 1990).  The residual is
-// formed as s*q0 - x so that x = -0 keeps its sign.
-__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
+// Correctly rounded x / d from y = RN(1/d) (Markstein's FMA-based quotient
+// correction; P. Markstein, IBM J. Res. Dev. 34(1), 1990), valid while the
+// residual does not underflow (see TileScale).  The residual is formed as
+// d*q0 - x so that x = -0 keeps its sign.
+__device__ __forceinline__ float div_by_scale(float x, float d, float y) {
   const float q0 = x * y;
-  const float r = __builtin_fmaf(s, q0, -x);
+  const float r = __builtin_fmaf(d, q0, -x);
   return __builtin_fmaf(-r, y, q0);
+}
+
+// x / s under either rule (RULE 0: amax, 1: power of two).
+template <int RULE>
+__device__ __forceinline__ float quotient(float x, const TileScale& t) {
+  if constexpr (RULE == 0) {
+    return div_by_scale(x * t.pre, t.d, t.y);
+  } else {
+    return x * t.y;
+  }
 }
 
 // Four fp32 values -> four E4M3 bytes (first value in the lowest byte),

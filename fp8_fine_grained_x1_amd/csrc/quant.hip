@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
       const TileScale sc = RULE == 0 ? scale_amax(m) : scale_pow2(m);
       float qv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = RULE == 0 ? div_by_scale(v[u][i], sc.s, sc.y) : v[u][i] * sc.y;
+      for (int i = 0; i < 8; ++i) qv[i] = quotient<RULE>(v[u][i], sc);
       uint2 out;
       out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
       out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
@@ -131,8 +131,7 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
     int64_t xs_ts, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_a,
     int64_t s_b) {
   __shared__ float part[16][128];
-  __shared__ float col_s[128];
-  __shared__ float col_y[128];
+  __shared__ TileScale col_sc[128];
   __shared__ uint32_t blk_max;
 
   const int tid = threadIdx.x;
@@ -156,7 +155,7 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
     }
   }
 
-  float ys[8], ss[8];
+  TileScale cs[8];
   if constexpr (PER_COLUMN) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -171,16 +170,12 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
 #pragma unroll
       for (int g = 1; g < 16; ++g) m = fmaxf(m, part[g][tid]);
       const TileScale sc = RULE == 0 ? scale_amax(m) : scale_pow2(m);
-      col_s[tid] = sc.s;
-      col_y[tid] = sc.y;
+      col_sc[tid] = sc;
       s[(c0 + tid) * s_a + (r0 >> 7) * s_b] = sc.s;
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ss[j] = col_s[cg * 8 + j];
-      ys[j] = col_y[cg * 8 + j];
-    }
+    for (int j = 0; j < 8; ++j) cs[j] = col_sc[cg * 8 + j];
   } else {
     float m = 0.0f;
 #pragma unroll
@@ -194,17 +189,14 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
     const TileScale sc = RULE == 0 ? scale_amax(__uint_as_float(blk_max)) : scale_pow2(__uint_as_float(blk_max));
     if (tid == 0) s[(r0 >> 7) * s_a + (c0 >> 7) * s_b] = sc.s;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ss[j] = sc.s;
-      ys[j] = sc.y;
-    }
+    for (int j = 0; j < 8; ++j) cs[j] = sc;
   }
 
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      v[i][j] = RULE == 0 ? div_by_scale(v[i][j], ss[j], ys[j]) : v[i][j] * ys[j];
+      v[i][j] = quotient<RULE>(v[i][j], cs[j]);
 
   if constexpr (TRANSPOSE) {
     // Output row c (an input column) is 128 contiguous bytes.  Stage the
