@@ -9,7 +9,9 @@
 // use power-of-two scales.
 //
 // Both kernels are HBM-streaming: each input element is read once and each
-// output byte written once.
+// output byte written once, with non-temporal loads and stores (nothing is
+// reused; streaming past the caches measured 5-12% faster than ordinary
+// accesses on the 4096 x 7168 activations).
 //
 // quant_1x128: 16 lanes own one tile (8 consecutive elements per lane, one
 //   16-byte load for bf16), so a wave reads 4 consecutive tiles = 1 KiB of
@@ -26,7 +28,8 @@
 //   maxima are reduced through LDS.  For the transposed layouts the bytes
 //   are converted directly in column order -- the conversion instruction
 //   takes any two registers -- and staged through LDS, so that each lane
-//   stores 16 contiguous bytes and a wave writes 8 whole 128-byte output rows.
+//   stores 16 contiguous bytes and a wave writes 8 whole 128-byte output rows;
+//   the staging buffer reuses the LDS of the column-max partials.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,6 +44,10 @@ constexpr int kQThreads = 256;
 constexpr int kGroupsPerBlock = kQThreads / 16;
 constexpr int kUnroll = 2;
 constexpr int kTPitch = 144;  // LDS row pitch (bytes) of the transposing store
+// 1x128 grid: up to 28 workgroups of 256 threads per CU (for the 4096 x 7168
+// activations exactly one pass of two tiles per lane group); 14 measured 10%
+// slower
+constexpr int k1x128BlocksPerCu = 28;
 
 // n / d for 32-bit n by multiply-high and shift (Granlund & Montgomery,
 // "Division by invariant integers using multiplication", PLDI 1994):
@@ -56,19 +63,42 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return (uint32_t)(t >> f.l);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Non-temporal 16- and 8-byte accesses.
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void st_nt8(void* p, uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 template <int XT>
 __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, float v[8]) {
   if constexpr (XT == 0) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
+    const uint4 w = ld_nt16(reinterpret_cast<const uint16_t*>(x) + off);
     v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
     v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
     v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
     v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const float* p = reinterpret_cast<const float*>(x) + off;
+    const uint4 a = ld_nt16(p), b = ld_nt16(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
   }
 }
 
@@ -107,7 +137,7 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
       uint2 out;
       out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
       out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
-      *reinterpret_cast<uint2*>(q + (int64_t)r[u] * ldq + tc[u] * 128 + lane16 * 8) = out;
+      st_nt8(q + (int64_t)r[u] * ldq + tc[u] * 128 + lane16 * 8, out);
       if (lane16 == 0) s[(int64_t)r[u] * s_rs + (int64_t)tc[u] * s_ts] = sc.s;
     }
   }
@@ -117,7 +147,7 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
 template <int XT>
 __device__ __forceinline__ void load_row8(const void* __restrict__ x, int64_t off, float v[8]) {
   if constexpr (XT == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(x) + off);
+    const uint2 w = ld_nt8(reinterpret_cast<const uint8_t*>(x) + off);
     unpack4_e4m3(w.x, v);
     unpack4_e4m3(w.y, v + 4);
   } else {
@@ -130,9 +160,14 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
     const void* __restrict__ x, int64_t ldx, const float* __restrict__ xs, int64_t xs_rs,
     int64_t xs_ts, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_a,
     int64_t s_b) {
-  __shared__ float part[16][128];
-  __shared__ TileScale col_sc[128];
+  static_assert(!PER_COLUMN || TRANSPOSE, "128x1 tiles are written transposed");
+  // The transposed store is staged in LDS; the column-max partials (16 x 128
+  // floats) use the first 8 KB of that buffer before it is written (two
+  // barriers separate their last read from the first staging write).
+  __shared__ __align__(16) uint8_t tbuf[TRANSPOSE ? 128 * kTPitch : 16];
+  __shared__ TileScale col_sc[PER_COLUMN ? 128 : 1];
   __shared__ uint32_t blk_max;
+  float (*part)[128] = reinterpret_cast<float (*)[128]>(tbuf);
 
   const int tid = threadIdx.x;
   const int cg = tid & 15;
@@ -204,7 +239,6 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
     // 8 whole rows: row pitch 144 bytes and 16-byte chunks XOR-swizzled by
     // (c / 16) % 8 keep the scattered 8-byte writes and the row reads off
     // the same LDS banks.
-    __shared__ __align__(16) uint8_t tbuf[128 * kTPitch];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint2 out;
@@ -221,7 +255,7 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
       const int c = k >> 3;
       const int chunk = k & 7;
       const uint4 w = *reinterpret_cast<const uint4*>(tbuf + c * kTPitch + ((chunk ^ ((c >> 4) & 7)) << 4));
-      *reinterpret_cast<uint4*>(q + (c0 + c) * ldq + r0 + chunk * 16) = w;
+      st_nt16(q + (c0 + c) * ldq + r0 + chunk * 16, w);
     }
   } else {
 #pragma unroll
@@ -229,7 +263,7 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
       uint2 out;
       out.x = pack4_e4m3(v[i][0], v[i][1], v[i][2], v[i][3]);
       out.y = pack4_e4m3(v[i][4], v[i][5], v[i][6], v[i][7]);
-      *reinterpret_cast<uint2*>(q + (r0 + rg * 8 + i) * ldq + c0 + cg * 8) = out;
+      st_nt8(q + (r0 + rg * 8 + i) * ldq + c0 + cg * 8, out);
     }
   }
 }
@@ -247,7 +281,7 @@ hipError_t launch_1x128_t(const RowtileArgs& a, hipStream_t st) {
   const int64_t ntiles = a.rows * tpr;
   const int64_t per_block = kGroupsPerBlock * kUnroll;
   const int64_t want = (ntiles + per_block - 1) / per_block;
-  const int64_t cap = (int64_t)device_cu_count() * 14;
+  const int64_t cap = (int64_t)device_cu_count() * k1x128BlocksPerCu;
   const int64_t blocks = want < cap ? want : cap;
   hipLaunchKernelGGL((quant_1x128_kernel<XT, RULE>), dim3((unsigned)blocks), dim3(kQThreads), 0, st,
                      a.x, (uint32_t)ntiles, make_fast_div((uint32_t)tpr), a.ldx, a.q, a.ldq, a.s,
@@ -265,10 +299,8 @@ hipError_t launch_t128_t(const Tile128Args& a, hipStream_t st) {
 
 template <int XT, int RULE>
 hipError_t dispatch_t128_layout(const Tile128Args& a, hipStream_t st) {
-  if (a.per_column) {
-    return a.transpose ? launch_t128_t<XT, RULE, true, true>(a, st)
-                       : launch_t128_t<XT, RULE, true, false>(a, st);
-  }
+  // 128x1 tiles are always written transposed (the ABI offers no other form)
+  if (a.per_column) return launch_t128_t<XT, RULE, true, true>(a, st);
   return a.transpose ? launch_t128_t<XT, RULE, false, true>(a, st)
                      : launch_t128_t<XT, RULE, false, false>(a, st);
 }
