@@ -102,13 +102,41 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, f
   }
 }
 
-// Tiles are numbered row-major (t = r * tiles_per_row + tc); lane group g of
-// the grid handles tiles g, g + G, ... (G = number of lane groups), two per
-// iteration so that both loads are in flight before either is processed.
-template <int XT, int RULE>
+// Lane group g of the grid handles tiles g, g + G, ... (G = number of lane
+// groups), two per iteration so that both loads are in flight before either
+// is processed.  ORDER 0 numbers the tiles row-major (t = r * tiles_per_row
+// + tc): a wave's four tiles lie side by side in one row, and with
+// row-major scales (s_ts = 1) their four scales are one 16-byte store.
+// ORDER 1, for scales stored group-major (s_rs = 1), numbers them in bands
+// of 16 rows, tile column by tile column (t = 16 tpr band + 16 tc + r % 16):
+// a wave's four tiles are four consecutive rows of one tile column, whose
+// scales are adjacent; the last band may have fewer rows.  (Scattered
+// 4-byte scale stores cost 20% more written bytes than the output itself.)
+template <int ORDER>
+__device__ __forceinline__ void tile_rc(uint32_t t, const FastDiv& tpr, const FastDiv& band,
+                                        uint32_t rows, uint32_t& r, uint32_t& tc) {
+  if constexpr (ORDER == 0) {
+    r = fast_div(t, tpr);
+    tc = t - r * tpr.d;
+  } else {
+    const uint32_t b = fast_div(t, band);
+    const uint32_t u = t - b * band.d;
+    const uint32_t h = rows - 16u * b;  // rows in this band (16 except in the last)
+    if (h >= 16u) {
+      tc = u >> 4;
+      r = 16u * b + (u & 15u);
+    } else {
+      tc = u / h;
+      r = 16u * b + (u - tc * h);
+    }
+  }
+}
+
+template <int XT, int RULE, int ORDER>
 __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
-    const void* __restrict__ x, uint32_t ntiles, FastDiv tpr, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_rs, int64_t s_ts) {
+    const void* __restrict__ x, uint32_t ntiles, FastDiv tpr, FastDiv band, uint32_t rows,
+    int64_t ldx, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_rs,
+    int64_t s_ts) {
   const int lane16 = threadIdx.x & 15;
   const uint32_t group = blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
   const uint32_t ngroups = gridDim.x * kGroupsPerBlock;
@@ -119,9 +147,10 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t t = t0 + u * ngroups;
-      r[u] = fast_div(t, tpr);
-      tc[u] = t - r[u] * tpr.d;
-      if (t < ntiles) load8<XT>(x, (int64_t)r[u] * ldx + tc[u] * 128 + lane16 * 8, v[u]);
+      if (t < ntiles) {
+        tile_rc<ORDER>(t, tpr, band, rows, r[u], tc[u]);
+        load8<XT>(x, (int64_t)r[u] * ldx + tc[u] * 128 + lane16 * 8, v[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -283,9 +312,18 @@ hipError_t launch_1x128_t(const RowtileArgs& a, hipStream_t st) {
   const int64_t want = (ntiles + per_block - 1) / per_block;
   const int64_t cap = (int64_t)device_cu_count() * k1x128BlocksPerCu;
   const int64_t blocks = want < cap ? want : cap;
-  hipLaunchKernelGGL((quant_1x128_kernel<XT, RULE>), dim3((unsigned)blocks), dim3(kQThreads), 0, st,
-                     a.x, (uint32_t)ntiles, make_fast_div((uint32_t)tpr), a.ldx, a.q, a.ldq, a.s,
-                     a.s_rs, a.s_ts);
+  const FastDiv fd_tpr = make_fast_div((uint32_t)tpr);
+  const FastDiv fd_band = make_fast_div((uint32_t)(16 * tpr));
+  // (the band order needs 16 * tiles_per_row < 2^32)
+  if (a.s_rs == 1 && tpr < ((int64_t)1 << 28)) {
+    hipLaunchKernelGGL((quant_1x128_kernel<XT, RULE, 1>), dim3((unsigned)blocks), dim3(kQThreads), 0, st,
+                       a.x, (uint32_t)ntiles, fd_tpr, fd_band, (uint32_t)a.rows, a.ldx, a.q, a.ldq, a.s,
+                       a.s_rs, a.s_ts);
+  } else {
+    hipLaunchKernelGGL((quant_1x128_kernel<XT, RULE, 0>), dim3((unsigned)blocks), dim3(kQThreads), 0, st,
+                       a.x, (uint32_t)ntiles, fd_tpr, fd_band, (uint32_t)a.rows, a.ldx, a.q, a.ldq, a.s,
+                       a.s_rs, a.s_ts);
+  }
   return hipGetLastError();
 }
 
