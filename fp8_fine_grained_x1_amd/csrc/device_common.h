@@ -97,6 +97,25 @@ __device__ __forceinline__ float quotient(float x, const TileScale& t) {
   }
 }
 
+// x / s for 8 values with one scale per lane.  Under the amax rule the
+// pre-scaling multiply is skipped when no active lane of the wave has a tiny
+// scale (a wave-uniform branch; there it is a multiply by 1).
+template <int RULE>
+__device__ __forceinline__ void quotient8(float (&v)[8], const TileScale& t) {
+  if constexpr (RULE == 0) {
+    if (__builtin_amdgcn_ballot_w64(t.pre != 1.0f) == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = div_by_scale(v[i], t.d, t.y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = div_by_scale(v[i] * t.pre, t.d, t.y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * t.y;
+  }
+}
+
 // Four fp32 values -> four E4M3 bytes (first value in the lowest byte),
 // round-to-nearest-even; values are clamped to +-448 first (saturation).
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {

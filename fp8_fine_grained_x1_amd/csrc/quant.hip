@@ -23,8 +23,8 @@
 //
 // quant_tile128: one 256-thread workgroup per 128x128 block.  Thread
 //   (rg, cg) = (tid / 16, tid % 16) holds rows 8rg..8rg+7 x columns
-//   8cg..8cg+7 in registers; a row of the block is read by 16 consecutive
-//   lanes (fully used 256-byte segments for bf16).  Column (128x1) or block
+//   8cg..8cg+7 in registers, undecoded; a row of the block is read by 16
+//   consecutive lanes (fully used 256-byte segments for bf16).  Column (128x1) or block
 //   maxima are reduced through LDS.  For the transposed layouts the bytes
 //   are converted directly in column order -- the conversion instruction
 //   takes any two registers -- and staged through LDS, so that each lane
@@ -32,6 +32,8 @@
 //   the staging buffer reuses the LDS of the column-max partials.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -162,7 +164,8 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
       const TileScale sc = RULE == 0 ? scale_amax(m) : scale_pow2(m);
       float qv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = quotient<RULE>(v[u][i], sc);
+      for (int i = 0; i < 8; ++i) qv[i] = v[u][i];
+      quotient8<RULE>(qv, sc);
       uint2 out;
       out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
       out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
@@ -173,19 +176,94 @@ __global__ __launch_bounds__(kQThreads) void quant_1x128_kernel(
 }
 
 // ---------------------------------------------------------------- 128 x 128
+// A thread's 8 x 8 elements stay in registers in their input encoding (bf16
+// pairs, f32, or E4M3 bytes) and are decoded where they are used: once for
+// the maxima and once for the quotients.  That keeps the kernel at 8
+// workgroups per CU (at most 64 VGPRs), where holding 64 decoded floats
+// allowed 5-6; the requantizer's 1792-block grid then fits in one round on
+// 256 CUs.  An f32 input is its own decoded form (64 VGPRs of raw data), so
+// that instantiation keeps the compiler's default register budget.
 template <int XT>
-__device__ __forceinline__ void load_row8(const void* __restrict__ x, int64_t off, float v[8]) {
-  if constexpr (XT == 2) {
-    const uint2 w = ld_nt8(reinterpret_cast<const uint8_t*>(x) + off);
-    unpack4_e4m3(w.x, v);
-    unpack4_e4m3(w.y, v + 4);
+struct RawRow;
+template <>
+struct RawRow<0> {  // 8 bf16
+  uint4 w;
+};
+template <>
+struct RawRow<1> {  // 8 f32
+  uint4 a, b;
+};
+template <>
+struct RawRow<2> {  // 8 E4M3 bytes
+  uint2 w;
+};
+
+template <int XT>
+__device__ __forceinline__ RawRow<XT> load_raw(const void* __restrict__ x, int64_t off) {
+  RawRow<XT> r;
+  if constexpr (XT == 0) {
+    r.w = ld_nt16(reinterpret_cast<const uint16_t*>(x) + off);
+  } else if constexpr (XT == 1) {
+    const float* p = reinterpret_cast<const float*>(x) + off;
+    r.a = ld_nt16(p);
+    r.b = ld_nt16(p + 4);
   } else {
-    load8<XT>(x, off, v);
+    r.w = ld_nt8(reinterpret_cast<const uint8_t*>(x) + off);
+  }
+  return r;
+}
+
+// Elements J and J + 1 (J even) of a raw row, exactly as fp32.
+template <int J, int XT>
+__device__ __forceinline__ void raw_pair(const RawRow<XT>& r, float& a, float& b) {
+  static_assert(J % 2 == 0 && J < 8, "pairs start at even columns");
+  if constexpr (XT == 0) {
+    const uint32_t w = J == 0 ? r.w.x : J == 2 ? r.w.y : J == 4 ? r.w.z : r.w.w;
+    a = bf16_lo(w);
+    b = bf16_hi(w);
+  } else if constexpr (XT == 1) {
+    const uint4& h = J < 4 ? r.a : r.b;
+    a = __uint_as_float((J & 3) == 0 ? h.x : h.z);
+    b = __uint_as_float((J & 3) == 0 ? h.y : h.w);
+  } else {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)(J < 4 ? r.w.x : r.w.y), (J & 2) != 0);
+    a = f[0];
+    b = f[1];
   }
 }
 
+// Hides a raw row's registers from the optimizer (no instruction is
+// emitted): the values decoded before this point cannot be reused after it,
+// so the second pass decodes again instead of keeping 64 floats live.
+template <int XT>
+__device__ __forceinline__ void refresh(RawRow<XT>& r) {
+  if constexpr (XT == 0) {
+    asm volatile("" : "+v"(r.w.x), "+v"(r.w.y), "+v"(r.w.z), "+v"(r.w.w));
+  } else if constexpr (XT == 1) {
+    asm volatile("" : "+v"(r.a.x), "+v"(r.a.y), "+v"(r.a.z), "+v"(r.a.w));
+    asm volatile("" : "+v"(r.b.x), "+v"(r.b.y), "+v"(r.b.z), "+v"(r.b.w));
+  } else {
+    asm volatile("" : "+v"(r.w.x), "+v"(r.w.y));
+  }
+}
+
+template <int J>
+struct ColTag {
+  static constexpr int value = J;
+};
+template <typename F, int... P>
+__device__ __forceinline__ void for_pairs_impl(F&& f, std::integer_sequence<int, P...>) {
+  (f(ColTag<2 * P>{}), ...);
+}
+// f(ColTag<0>{}), f(ColTag<2>{}), .. f(ColTag<6>{}): the first column of
+// each pair as a compile-time constant.
+template <typename F>
+__device__ __forceinline__ void for_pairs(F&& f) {
+  for_pairs_impl(f, std::make_integer_sequence<int, 4>{});
+}
+
 template <int XT, int RULE, bool PER_COLUMN, bool TRANSPOSE>
-__global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
+__global__ __launch_bounds__(kQThreads, XT == 1 ? 1 : 8) void quant_tile128_kernel(
     const void* __restrict__ x, int64_t ldx, const float* __restrict__ xs, int64_t xs_rs,
     int64_t xs_ts, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_a,
     int64_t s_b) {
@@ -206,28 +284,39 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
 
   if (!PER_COLUMN && tid == 0) blk_max = 0u;
 
-  float v[8][8];
+  RawRow<XT> raw[8];
+  float rsc[8];  // requantization: the input scale of each row
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = r0 + rg * 8 + i;
-    load_row8<XT>(x, row * ldx + c0 + cg * 8, v[i]);
-    if constexpr (XT == 2) {
-      // requantization source: RN32(dec(q1) * s1), one input scale per row
-      const float sc = xs[row * xs_rs + (c0 >> 7) * xs_ts];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * sc;
-    }
+    raw[i] = load_raw<XT>(x, row * ldx + c0 + cg * 8);
+    if constexpr (XT == 2) rsc[i] = xs[row * xs_rs + (c0 >> 7) * xs_ts];
   }
-
-  TileScale cs[8];
-  if constexpr (PER_COLUMN) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float m = fabsf(v[0][j]);
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[i][j]));
-      part[rg][cg * 8 + j] = m;
+  // elements (i, J) and (i, J + 1) of the thread's block; for
+  // requantization RN32(dec(q1) * s1)
+  auto pair = [&](int i, auto col, float& a, float& b) {
+    raw_pair<decltype(col)::value>(raw[i], a, b);
+    if constexpr (XT == 2) {
+      a *= rsc[i];
+      b *= rsc[i];
     }
+  };
+
+  TileScale bsc{};  // the block's scale (128x128 tiles)
+  if constexpr (PER_COLUMN) {
+    for_pairs([&](auto col) {
+      float ma = 0.0f, mb = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        float a0, b0, a1, b1;
+        pair(i, col, a0, b0);
+        pair(i + 1, col, a1, b1);
+        ma = fmaxf(fmaxf(ma, fabsf(a0)), fabsf(a1));  // one three-input max
+        mb = fmaxf(fmaxf(mb, fabsf(b0)), fabsf(b1));
+      }
+      part[rg][cg * 8 + decltype(col)::value] = ma;
+      part[rg][cg * 8 + decltype(col)::value + 1] = mb;
+    });
     __syncthreads();
     if (tid < 128) {
       float m = part[0][tid];
@@ -238,45 +327,55 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
       s[(c0 + tid) * s_a + (r0 >> 7) * s_b] = sc.s;
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cs[j] = col_sc[cg * 8 + j];
   } else {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
+      for_pairs([&](auto col) {
+        float a, b;
+        pair(i, col, a, b);
+        m = fmaxf(fmaxf(m, fabsf(a)), fabsf(b));  // one three-input max
+      });
     m = row16_max(m);
     __syncthreads();  // blk_max initialised
     if ((tid & 15) == 0) atomicMax(&blk_max, __float_as_uint(m));  // m >= 0: integer order == float order
     __syncthreads();
-    const TileScale sc = RULE == 0 ? scale_amax(__uint_as_float(blk_max)) : scale_pow2(__uint_as_float(blk_max));
-    if (tid == 0) s[(r0 >> 7) * s_a + (c0 >> 7) * s_b] = sc.s;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cs[j] = sc;
+    bsc = RULE == 0 ? scale_amax(__uint_as_float(blk_max)) : scale_pow2(__uint_as_float(blk_max));
+    if (tid == 0) s[(r0 >> 7) * s_a + (c0 >> 7) * s_b] = bsc.s;
   }
-
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[i][j] = quotient<RULE>(v[i][j], cs[j]);
+  for (int i = 0; i < 8; ++i) refresh(raw[i]);
 
   if constexpr (TRANSPOSE) {
     // Output row c (an input column) is 128 contiguous bytes.  Stage the
     // block through LDS so that every lane stores 16 bytes and a wave writes
     // 8 whole rows: row pitch 144 bytes and 16-byte chunks XOR-swizzled by
     // (c / 16) % 8 keep the scattered 8-byte writes and the row reads off
-    // the same LDS banks.
+    // the same LDS banks.  The bytes are formed a pair of columns at a
+    // time: the conversion instruction takes any two registers.
+    for_pairs([&](auto col) {
+      constexpr int J = decltype(col)::value;
+      float va[8], vb[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint2 out;
-      out.x = pack4_e4m3(v[0][j], v[1][j], v[2][j], v[3][j]);
-      out.y = pack4_e4m3(v[4][j], v[5][j], v[6][j], v[7][j]);
-      const int c = cg * 8 + j;
-      const int chunk = (rg >> 1) ^ ((c >> 4) & 7);
-      *reinterpret_cast<uint2*>(tbuf + c * kTPitch + chunk * 16 + (rg & 1) * 8) = out;
-    }
+      for (int i = 0; i < 8; ++i) pair(i, col, va[i], vb[i]);
+      TileScale ca = bsc, cb = bsc;
+      if constexpr (PER_COLUMN) {
+        ca = col_sc[cg * 8 + J];
+        cb = col_sc[cg * 8 + J + 1];
+      }
+      quotient8<RULE>(va, ca);
+      quotient8<RULE>(vb, cb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* v = h ? vb : va;
+        const int c = cg * 8 + J + h;
+        uint2 out;
+        out.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+        out.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
+        const int chunk = (rg >> 1) ^ ((c >> 4) & 7);
+        *reinterpret_cast<uint2*>(tbuf + c * kTPitch + chunk * 16 + (rg & 1) * 8) = out;
+      }
+    });
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -289,9 +388,12 @@ __global__ __launch_bounds__(kQThreads) void quant_tile128_kernel(
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      float v[8];
+      for_pairs([&](auto col) { pair(i, col, v[decltype(col)::value], v[decltype(col)::value + 1]); });
+      quotient8<RULE>(v, bsc);
       uint2 out;
-      out.x = pack4_e4m3(v[i][0], v[i][1], v[i][2], v[i][3]);
-      out.y = pack4_e4m3(v[i][4], v[i][5], v[i][6], v[i][7]);
+      out.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+      out.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
       st_nt8(q + (r0 + rg * 8 + i) * ldq + c0 + cg * 8, out);
     }
   }
