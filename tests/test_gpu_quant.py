@@ -172,7 +172,60 @@ def test_128x1_f32_input():
     assert np.array_equal(host(st), so.T) and np.array_equal(host(qt), qo.T)
 
 
+def _tiny_mixed(rows, cols, seed):
+    """Columns (and 128x128 blocks) whose scales fall below 2^-64 -- where
+    the quotient is formed from operands scaled by 2^64 -- next to normal,
+    zero and subnormal ones, so that one wave holds both kinds."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    colscale = np.ones(cols, np.float32)
+    colscale[0::4] = np.float32(1e-25)   # amax / 448 ~ 1e-27 < 2^-64
+    colscale[1::8] = np.float32(3e-36)   # scale near the 2^-126 floor
+    colscale[3::16] = np.float32(0.0)    # all-zero columns
+    x *= colscale
+    x[:, 5::16] = np.float32(1e-39) * np.arange(rows, dtype=np.float32)[:, None]  # subnormal
+    x[: rows // 2, cols // 2:] *= np.float32(1e-22)  # tiny 128x128 blocks
+    return x
+
+
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_128x1_tiny_and_mixed_scales(pow2, rule):
+    x = _tiny_mixed(256, 512, seed=41)
+    for xin in (f32_dev(x), bf16_dev(workloads.f32_to_bf16_bits(x))):
+        xo = x if xin.dtype == torch.float32 else f32(workloads.f32_to_bf16_bits(x))
+        qt, st = T.quantize_128x1(xin, pow2=pow2)
+        qo, so = oracle.quantize_128x1(xo, rule)
+        assert np.any(so < 2.0 ** -64) and np.any(so >= 1e-3)
+        assert np.array_equal(host(st), so.T) and np.array_equal(host(qt), qo.T)
+
+
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_128x1_requant_tiny_and_mixed_scales(pow2, rule):
+    bits = workloads.f32_to_bf16_bits(_tiny_mixed(256, 512, seed=43))
+    q1, s1 = T.quantize_1x128(bf16_dev(bits))
+    q1o, s1o = oracle.quantize_1x128(f32(bits))
+    assert np.array_equal(host(q1), q1o) and np.array_equal(host(s1), s1o)
+    qt, st = T.requantize_128x1(q1, s1, pow2=pow2)
+    qo, so = oracle.requantize_128x1(q1o, s1o, rule)
+    assert np.any(so < 2.0 ** -64)
+    assert np.array_equal(host(st), so.T) and np.array_equal(host(qt), qo.T)
+
+
 # ---------------------------------------------------------------- 128x128
+@pytest.mark.parametrize("transpose", [True, False])
+@pytest.mark.parametrize("pow2,rule", RULES)
+def test_block_tiny_blocks(transpose, pow2, rule):
+    x = _tiny_mixed(256, 512, seed=47)
+    x[128:, :128] = np.float32(1e-30) * x[128:, :128] / np.float32(max(1e-30, np.abs(x[128:, :128]).max()))
+    for xin in (f32_dev(x), bf16_dev(workloads.f32_to_bf16_bits(x))):
+        xo = x if xin.dtype == torch.float32 else f32(workloads.f32_to_bf16_bits(x))
+        q, s = T.quantize_block(xin, pow2=pow2, transpose=transpose)
+        qo, so = oracle.quantize_128x128(xo, rule)
+        assert np.any(so < 2.0 ** -64) and np.any(so > 2.0 ** -64)
+        assert np.array_equal(host(s), so)
+        assert np.array_equal(host(q), qo.T if transpose else qo)
+
+
 @pytest.mark.parametrize("transpose", [True, False])
 @pytest.mark.parametrize("pow2,rule", RULES)
 @pytest.mark.parametrize("rows,cols", [(128, 128), (512, 256), (256, 640)])
