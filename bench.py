@@ -36,7 +36,11 @@ carry a back-to-back figure (one event pair around 40 calls over >= 1 GiB
 of rotated sets): an event pair around every launch adds its dispatch gap,
 about 3 us, to a kernel of about 20 us.  `hbm_copy_context` times a plain 1 GiB device copy
 in the same run: the HBM rate a pure stream reaches here, beside which the
-quantizers' fractions of the published 8 TB/s are to be read.
+quantizers' fractions of the published 8 TB/s are to be read;
+`vendor_gemm_context` times the vendor library's FP8 GEMM (per-tensor and
+row/column scales, no per-K-group promotion) and BF16 GEMM on the dense
+forward shape, beside which the GEMM's fraction of the FP8 peak is to be
+read.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 200] [--settle-ms 500]
     python bench.py --copy-calibration   # plain 1 GiB device copy, for the
@@ -619,13 +623,61 @@ def outside_step(env):
     cp_dst = torch.empty_like(cp_src)
     cp_ms = timed([lambda: cp_dst.copy_(cp_src)], reps=10)
     del cp_src, cp_dst
+    progress("copy context timed")
+    vendor = vendor_gemm_context(timed, nbytes, n_sets, tflops)
+    progress("vendor GEMM context timed")
     return {
         "kernels": kernels,
         "hbm_copy_context": {
             "1 GiB device copy GB/s (read + write)": round(gbs(2 * (1 << 30), cp_ms), 1),
             "frac_hbm": round(gbs(2 * (1 << 30), cp_ms) / PEAK_HBM_GBS, 3)},
+        "vendor_gemm_context": vendor,
         "error_context": error_context,
     }
+
+
+def vendor_gemm_context(timed, nbytes, n_sets, tflops):
+    """The vendor library (hipBLASLt through torch) on the dense forward
+    shape 4096 x 7168 x 7168, same run, rotated operand sets: its FP8 GEMM
+    with one scale per tensor and with one scale per row of A and column of
+    B (no per-K-group scaling, accumulated inside the FP8 matrix core over
+    the whole K), and its BF16 GEMM.  They show what the matrix cores deliver
+    on this shape under the chip's power limit; none of them is the method
+    (the first two are the un-promoted kind of accumulation whose error the
+    method removes)."""
+    import torch
+    dev = torch.device("cuda:0")
+    M, N, K = 4096, 7168, 7168
+    g = torch.Generator(device=dev).manual_seed(5)
+    a = torch.randn(M, K, generator=g, device=dev).to(torch.float8_e4m3fn)
+    b = (torch.randn(N, K, generator=g, device=dev) * 9.0).to(torch.float8_e4m3fn)
+    out = {}
+    flops = 2.0 * M * N * K
+    try:
+        base = dict(a=a, b=b, c=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+        sets = [base] + [{k: v.clone() for k, v in base.items()}
+                         for _ in range(n_sets(nbytes(*base.values())) - 1)]
+        one = torch.ones((), device=dev)
+        ra, rb = torch.ones((M, 1), device=dev), torch.ones((1, N), device=dev)
+        ms = timed([lambda s=s: torch._scaled_mm(s["a"], s["b"].t(), scale_a=one, scale_b=one,
+                                                 out_dtype=torch.bfloat16, out=s["c"]) for s in sets])
+        out["fp8 per-tensor scales, TFLOP/s"] = round(tflops(flops, ms), 1)
+        ms = timed([lambda s=s: torch._scaled_mm(s["a"], s["b"].t(), scale_a=ra, scale_b=rb,
+                                                 out_dtype=torch.bfloat16, out=s["c"]) for s in sets])
+        out["fp8 row/column scales, TFLOP/s"] = round(tflops(flops, ms), 1)
+        del sets, base
+    except (RuntimeError, TypeError) as e:  # no FP8 GEMM in this torch build
+        out["fp8"] = "unavailable: %s" % str(e)[:120]
+    del a, b
+    a = torch.randn(M, K, generator=g, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, generator=g, device=dev, dtype=torch.bfloat16)
+    base = dict(a=a, b=b, c=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+    sets = [base] + [{k: v.clone() for k, v in base.items()}
+                     for _ in range(n_sets(nbytes(*base.values())) - 1)]
+    ms = timed([lambda s=s: torch.matmul(s["a"], s["b"], out=s["c"]) for s in sets])
+    out["bf16, TFLOP/s"] = round(tflops(flops, ms), 1)
+    out["fp8 peak TFLOP/s"] = PEAK_FP8_TFLOPS
+    return out
 
 
 def long_k_error_gap(a3, b3, qa3, sa3, qb3, sb3, rel_err):
