@@ -976,10 +976,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_kernel(KParams p) {
       emax[i][j] = -(1 << 20);
     }
 
-  // Top of group kb: the copies issued in group kb - 1 (this group's data)
-  // are the newest memory operations, so wait for all; after the barrier
-  // every wave's copies have landed and every wave has finished reading the
-  // other stage.
+  // Top of group kb (team 0; team 1 waits at its step 4, see the group
+  // below): the copies issued in group kb - 1 (this group's data) are the
+  // newest memory operations, so wait for all; after the barrier every
+  // wave's copies of this group have landed and every wave has finished
+  // reading the other stage.
   auto wait_group = [&]() {
     wait_vmcnt<0>();
     block_barrier();
@@ -1419,10 +1420,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rescale_grouped_kernel(KPara
         emax[i][j] = -(1 << 20);
       }
 
-    // Top of group kb: the copies issued in group kb - 1 (this group's data)
-    // are the newest memory operations, so wait for all; after the barrier
-    // every wave's copies have landed and every wave has finished reading the
-    // other stage.
+    // Top of group kb (team 0; team 1 waits at its step 4): the copies
+    // issued in group kb - 1 (this group's data) are the newest memory
+    // operations, so wait for all; after the barrier every wave's copies of
+    // this group have landed and every wave has finished reading the other
+    // stage.
     auto wait_group = [&]() {
       wait_vmcnt<0>();
       block_barrier();
