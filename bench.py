@@ -35,8 +35,10 @@ before 20 timed calls.  The quantizers, in the step and outside it, also
 carry a back-to-back figure (one event pair around 40 calls over >= 1 GiB
 of rotated sets): an event pair around every launch adds its dispatch gap,
 about 3 us, to a kernel of about 20 us.  `hbm_copy_context` times a plain 1 GiB device copy
-in the same run: the HBM rate a pure stream reaches here, beside which the
-quantizers' fractions of the published 8 TB/s are to be read;
+and torch's own bf16 -> E4M3 cast of the step's activations in the same run:
+the HBM rates a pure stream and a stream with the 1x128 quantizer's
+read/write mix reach here, beside which the quantizers' fractions of the
+published 8 TB/s are to be read;
 `vendor_gemm_context` times the vendor library's FP8 GEMM (per-tensor and
 row/column scales, no per-K-group promotion) and BF16 GEMM on the dense
 forward shape, beside which the GEMM's fraction of the FP8 peak is to be
@@ -623,6 +625,14 @@ def outside_step(env):
     cp_dst = torch.empty_like(cp_src)
     cp_ms = timed([lambda: cp_dst.copy_(cp_src)], reps=10)
     del cp_src, cp_dst
+    # ... and torch's own cast of the step's activations to E4M3 (2 bytes in,
+    # 1 out per element, no maxima or scales): a stream with the 1x128
+    # quantizer's read/write mix
+    cast_base = dict(a=st0["a"], o=torch.empty(st0["a"].shape, dtype=torch.float8_e4m3fn, device=dev))
+    cast_sets = clones(cast_base, n_sets(nbytes(*cast_base.values())))
+    cast_ms = env["timed_batch"]([lambda s=s: s["o"].copy_(s["a"]) for s in cast_sets])
+    cast_bytes = st0["a"].numel() * 3
+    del cast_sets, cast_base
     progress("copy context timed")
     vendor = vendor_gemm_context(timed, nbytes, n_sets, tflops)
     progress("vendor GEMM context timed")
@@ -630,7 +640,10 @@ def outside_step(env):
         "kernels": kernels,
         "hbm_copy_context": {
             "1 GiB device copy GB/s (read + write)": round(gbs(2 * (1 << 30), cp_ms), 1),
-            "frac_hbm": round(gbs(2 * (1 << 30), cp_ms) / PEAK_HBM_GBS, 3)},
+            "frac_hbm": round(gbs(2 * (1 << 30), cp_ms) / PEAK_HBM_GBS, 3),
+            "torch bf16 -> float8_e4m3fn cast of the 4096x7168 activations GB/s (back to back)":
+                round(gbs(cast_bytes, cast_ms), 1),
+            "cast_frac_hbm": round(gbs(cast_bytes, cast_ms) / PEAK_HBM_GBS, 3)},
         "vendor_gemm_context": vendor,
         "error_context": error_context,
     }
